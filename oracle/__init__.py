@@ -1,0 +1,234 @@
+"""CPU oracle for MXFP8 quantization and the block-scaled grouped GEMM.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product path
+(the HIP library ``libmxmoe`` and its Python binding) never imports it, and the
+two share no code.
+
+The arithmetic lives in ``mxref.c`` (plain C, double precision, exact steps);
+this module only builds it with gcc and marshals numpy arrays through ctypes.
+The definitions follow the public write-ups on Cursor's Blackwell MoE kernels
+(aigc.bar "被忽视的量化税"/"秘密武器"; lpnh.cn 2479732 section 1); the readings
+of what the pages leave open are stated in ``mxref.c``.
+
+Parity status of each function (what pins it in ``tests/test_oracle.py``):
+  e4m3_encode / quantize_with_scale  exhaustive vs an independent table-search
+                                     encoder over every finite bf16 x every S
+  block_scale                        exhaustive closed form over every amax
+  quantize_rows / quantize_cols      hand-worked blocks (tests/golden), invariants,
+                                     cols == rows of the transposed group slices
+  pack / unpack_scales               hand-computed offsets (tests/golden)
+  grouped_gemm(_points)              exact rational brute force on small shapes,
+                                     one-hot closed form
+  wgrad(_points)                     exact rational brute force on small shapes
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mxref.c")
+_LIB_PATH = os.path.join(_HERE, "libmxref.so")
+_lib = None
+
+
+def build(force=False):
+    """Compile mxref.c into oracle/libmxref.so with gcc (plain -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < max(
+        os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "mxref.h"))
+    ):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-Wall", "-fPIC",
+             "-shared", _SRC, "-o", tmp, "-lm"]
+        )
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = os.environ.get("MXREF_LIB")  # a test may point at a deliberately broken build
+    if not path:
+        path = build()
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.mxref_bf16_value.argtypes = [ctypes.c_uint16]
+    lib.mxref_bf16_value.restype = ctypes.c_double
+    lib.mxref_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.mxref_e4m3_value.restype = ctypes.c_double
+    lib.mxref_e4m3_encode.argtypes = [ctypes.c_double]
+    lib.mxref_e4m3_encode.restype = ctypes.c_uint8
+    lib.mxref_block_scale.argtypes = [P, I64, I64]
+    lib.mxref_block_scale.restype = ctypes.c_uint8
+    lib.mxref_quantize_with_scale.argtypes = [P, I64, ctypes.c_uint8, P]
+    lib.mxref_dequant.argtypes = [ctypes.c_uint8, ctypes.c_uint8]
+    lib.mxref_dequant.restype = ctypes.c_double
+    lib.mxref_quantize_rows.argtypes = [P, I64, I64, P, P]
+    lib.mxref_quantize_cols.argtypes = [P, I64, I64, P, ctypes.c_int32, I64, P, P, P]
+    lib.mxref_quantize_cols.restype = ctypes.c_int
+    lib.mxref_packed_scale_bytes.argtypes = [I64, I64]
+    lib.mxref_packed_scale_bytes.restype = I64
+    lib.mxref_pack_scales.argtypes = [P, I64, I64, P]
+    lib.mxref_unpack_scales.argtypes = [P, I64, I64, P]
+    lib.mxref_grouped_gemm.argtypes = [P, P, P, P, P, ctypes.c_int32, I64, I64, I64, P]
+    lib.mxref_grouped_gemm_points.argtypes = [P, P, P, P, P, ctypes.c_int32, I64, I64, I64, P, P, I64, P]
+    lib.mxref_wgrad.argtypes = [P, P, P, P, P, ctypes.c_int32, I64, I64, I64, P]
+    lib.mxref_wgrad_points.argtypes = [P, P, P, P, P, ctypes.c_int32, I64, I64, I64, P, P, P, I64, P]
+    _lib = lib
+    return lib
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def bf16_value(bits):
+    return _load().mxref_bf16_value(int(bits))
+
+
+def e4m3_value(code):
+    return _load().mxref_e4m3_value(int(code))
+
+
+def e4m3_encode(y):
+    return int(_load().mxref_e4m3_encode(float(y)))
+
+
+def block_scale(block_bits):
+    a, p = _c(block_bits, np.uint16)
+    return int(_load().mxref_block_scale(p, a.size, 1))
+
+
+def quantize_with_scale(x_bits, S):
+    a, p = _c(x_bits, np.uint16)
+    q = np.empty(a.size, np.uint8)
+    _load().mxref_quantize_with_scale(p, a.size, int(S), q.ctypes.data_as(ctypes.c_void_p))
+    return q.reshape(np.shape(x_bits))
+
+
+def dequant(q, S):
+    return _load().mxref_dequant(int(q), int(S))
+
+
+def quantize_rows(x_bits):
+    """bf16 bits [M, K] -> (codes uint8 [M, K], canonical scales uint8 [M, K/32])."""
+    x, p = _c(x_bits, np.uint16)
+    M, K = x.shape
+    assert K % 32 == 0
+    q = np.empty((M, K), np.uint8)
+    s = np.empty((M, K // 32), np.uint8)
+    _load().mxref_quantize_rows(p, M, K, q.ctypes.data_as(ctypes.c_void_p), s.ctypes.data_as(ctypes.c_void_p))
+    return q, s
+
+
+def cols_capacity(M, G):
+    return 256 * ((M + 255) // 256 + max(G, 1) - 1)
+
+
+def quantize_cols(x_bits, offsets=None, Mcap=None):
+    """bf16 bits [M, N] -> (qT [N, Mcap], canonical sT [N, Mcap/32], padded offsets [G+1])."""
+    x, p = _c(x_bits, np.uint16)
+    M, N = x.shape
+    if offsets is None:
+        G = 1
+        op = None
+    else:
+        off, op = _c(offsets, np.int32)
+        G = off.size - 1
+    if Mcap is None:
+        Mcap = cols_capacity(M, G)
+    qT = np.empty((N, Mcap), np.uint8)
+    sT = np.empty((N, Mcap // 32), np.uint8)
+    padded = np.empty(G + 1, np.int32)
+    rc = _load().mxref_quantize_cols(p, M, N, op, G, Mcap, qT.ctypes.data_as(ctypes.c_void_p),
+                                     sT.ctypes.data_as(ctypes.c_void_p), padded.ctypes.data_as(ctypes.c_void_p))
+    if rc != 0:
+        raise ValueError("Mcap too small")
+    return qT, sT, padded
+
+
+def packed_scale_bytes(R, K):
+    return int(_load().mxref_packed_scale_bytes(R, K))
+
+
+def pack_scales(s, K):
+    s, p = _c(s, np.uint8)
+    R = s.shape[0]
+    out = np.empty(packed_scale_bytes(R, K), np.uint8)
+    _load().mxref_pack_scales(p, R, K, out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def unpack_scales(packed, R, K):
+    pk, p = _c(packed, np.uint8)
+    s = np.empty((R, K // 32), np.uint8)
+    _load().mxref_unpack_scales(p, R, K, s.ctypes.data_as(ctypes.c_void_p))
+    return s
+
+
+def grouped_gemm(Xq, Xs, Wq, Ws, offsets):
+    """fp64 reference out [M, N]; Wq [G, N, K], Ws [G, N, K/32] canonical."""
+    Xq, px = _c(Xq, np.uint8)
+    Xs, pxs = _c(Xs, np.uint8)
+    Wq, pw = _c(Wq, np.uint8)
+    Ws, pws = _c(Ws, np.uint8)
+    off, po = _c(offsets, np.int32)
+    M, K = Xq.shape
+    G, N, _ = Wq.shape
+    out = np.empty((M, N), np.float64)
+    _load().mxref_grouped_gemm(px, pxs, pw, pws, po, G, M, N, K, out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def grouped_gemm_points(Xq, Xs, Wq, Ws, offsets, rows, cols):
+    Xq, px = _c(Xq, np.uint8)
+    Xs, pxs = _c(Xs, np.uint8)
+    Wq, pw = _c(Wq, np.uint8)
+    Ws, pws = _c(Ws, np.uint8)
+    off, po = _c(offsets, np.int32)
+    r, pr = _c(rows, np.int64)
+    c, pc = _c(cols, np.int64)
+    M, K = Xq.shape
+    G, N, _ = Wq.shape
+    out = np.empty(r.size, np.float64)
+    _load().mxref_grouped_gemm_points(px, pxs, pw, pws, po, G, M, N, K, pr, pc, r.size,
+                                      out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def wgrad(Aq, As, Bq, Bs, padded):
+    Aq, pa = _c(Aq, np.uint8)
+    As, pas = _c(As, np.uint8)
+    Bq, pb = _c(Bq, np.uint8)
+    Bs, pbs = _c(Bs, np.uint8)
+    P, pp = _c(padded, np.int32)
+    N, Mcap = Aq.shape
+    K = Bq.shape[0]
+    G = P.size - 1
+    dW = np.empty((G, N, K), np.float64)
+    _load().mxref_wgrad(pa, pas, pb, pbs, pp, G, N, K, Mcap, dW.ctypes.data_as(ctypes.c_void_p))
+    return dW
+
+
+def wgrad_points(Aq, As, Bq, Bs, padded, gs, ns, ks):
+    Aq, pa = _c(Aq, np.uint8)
+    As, pas = _c(As, np.uint8)
+    Bq, pb = _c(Bq, np.uint8)
+    Bs, pbs = _c(Bs, np.uint8)
+    P, pp = _c(padded, np.int32)
+    g, pg = _c(gs, np.int64)
+    n, pn = _c(ns, np.int64)
+    k, pk = _c(ks, np.int64)
+    N, Mcap = Aq.shape
+    K = Bq.shape[0]
+    out = np.empty(g.size, np.float64)
+    _load().mxref_wgrad_points(pa, pas, pb, pbs, pp, P.size - 1, N, K, Mcap, pg, pn, pk, g.size,
+                               out.ctypes.data_as(ctypes.c_void_p))
+    return out

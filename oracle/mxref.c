@@ -1,0 +1,276 @@
+/*
+ * mxref.c -- CPU oracle for MXFP8 (1x32 blocks, E4M3FN elements, E8M0
+ * scales) and the block-scaled grouped GEMM.  TEST INFRASTRUCTURE ONLY: the
+ * product path never links or calls this file.
+ *
+ * Written from the definitions in the public write-ups on Cursor's
+ * Blackwell MoE kernels (aigc.bar, "被忽视的量化税" and "秘密武器";
+ * lpnh.cn 2479732, section 1).  The pages say: cut the tensor into blocks of
+ * 32, compute one scale per block, divide the block by the scale, cast to
+ * FP8 E4M3.  They fix nothing else.  Readings taken here:
+ *   - scale byte S (E8M0, value 2^(S-127)) = clamp(floor(log2 amax) - 8,
+ *     -127, 127) + 127, amax = 0 counting as floor(log2 0) = -inf (S = 0);
+ *     8 is the exponent of the largest power of two in E4M3;
+ *   - elements: y = x * 2^(127-S) (exact), |y| saturated to 448, then
+ *     round-to-nearest-even on the OCP E4M3FN grid (bias 7, subnormal
+ *     quantum 2^-9, no infinities), sign kept also for zero;
+ *   - bf16 subnormals are exact inputs (never flushed);
+ *   - non-finite inputs are outside the contract.
+ * Arithmetic is double precision and every step is exact: ldexp/frexp scale
+ * by powers of two, nearbyint rounds to an integer with ties to even (the
+ * default FE_TONEAREST mode, asserted on every call that rounds).
+ */
+#include "mxref.h"
+#include <fenv.h>
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+static void require_rne(void) {
+    if (fegetround() != FE_TONEAREST) abort();
+}
+
+/* bf16 = the upper 16 bits of an IEEE binary32: sign, 8 exponent bits
+ * (bias 127), 7 fraction bits.  Decoded field by field, not by type punning,
+ * so that no float hardware (and no flush-to-zero) is involved. */
+double mxref_bf16_value(uint16_t bits) {
+    int sign = (bits >> 15) & 1;
+    int ef = (bits >> 7) & 0xFF;
+    int fr = bits & 0x7F;
+    double v;
+    if (ef == 0) {
+        v = ldexp((double)fr, -126 - 7);              /* subnormal: 0.f * 2^-126 */
+    } else if (ef == 0xFF) {
+        v = fr ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(128 + fr), ef - 127 - 7);  /* 1.f * 2^(e-127) */
+    }
+    return sign ? -v : v;
+}
+
+/* OCP E4M3FN: sign, 4 exponent bits (bias 7), 3 fraction bits; exponent
+ * field 0 is subnormal (0.f * 2^-6); S.1111.111 is NaN; no infinities. */
+double mxref_e4m3_value(uint8_t code) {
+    int sign = (code >> 7) & 1;
+    int ef = (code >> 3) & 0xF;
+    int fr = code & 7;
+    double v;
+    if (ef == 15 && fr == 7) return NAN;
+    if (ef == 0) v = ldexp((double)fr, -6 - 3);
+    else v = ldexp((double)(8 + fr), ef - 7 - 3);
+    return sign ? -v : v;
+}
+
+uint8_t mxref_e4m3_encode(double y) {
+    require_rne();
+    int neg = signbit(y) ? 1 : 0;
+    double a = fabs(y);
+    int code;
+    if (a > 448.0) a = 448.0;                /* saturate; 448 is on the grid */
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal range (and zero): multiples of 2^-9 */
+        code = (int)nearbyint(ldexp(a, 9));  /* 0..8; 8 is the smallest normal */
+    } else {
+        int e;
+        (void)frexp(a, &e);                  /* a = f * 2^e, f in [0.5, 1) */
+        int E = e - 1;                       /* floor(log2 a), -6..8 */
+        int n = (int)nearbyint(ldexp(a, 3 - E));  /* 8..16; 16 carries into E+1 */
+        code = ((E + 7) << 3) + (n - 8);
+    }
+    return (uint8_t)(code | (neg << 7));
+}
+
+uint8_t mxref_block_scale(const uint16_t* x, int64_t n, int64_t stride) {
+    double amax = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double a = fabs(mxref_bf16_value(x[i * stride]));
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0) return 0;               /* floor(log2 0) = -inf, clamped to -127 */
+    int e;
+    (void)frexp(amax, &e);
+    int shared = (e - 1) - 8;                /* floor(log2 amax) - emax(E4M3) */
+    if (shared < -127) shared = -127;
+    if (shared > 127) shared = 127;
+    return (uint8_t)(shared + 127);
+}
+
+void mxref_quantize_with_scale(const uint16_t* x, int64_t n, uint8_t S, uint8_t* q) {
+    for (int64_t i = 0; i < n; ++i) {
+        double y = ldexp(mxref_bf16_value(x[i]), 127 - (int)S);  /* x / 2^(S-127) */
+        q[i] = mxref_e4m3_encode(y);
+    }
+}
+
+double mxref_dequant(uint8_t q, uint8_t S) {
+    return ldexp(mxref_e4m3_value(q), (int)S - 127);
+}
+
+void mxref_quantize_rows(const uint16_t* x, int64_t M, int64_t K, uint8_t* q, uint8_t* s) {
+    int64_t nb = K / 32;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint16_t* blk = x + m * K + b * 32;
+            uint8_t S = mxref_block_scale(blk, 32, 1);
+            s[m * nb + b] = S;
+            mxref_quantize_with_scale(blk, 32, S, q + m * K + b * 32);
+        }
+    }
+}
+
+int mxref_quantize_cols(const uint16_t* x, int64_t M, int64_t N, const int32_t* off, int32_t G,
+                        int64_t Mcap, uint8_t* qT, uint8_t* sT, int32_t* padded) {
+    int32_t one_group[2];
+    if (off == NULL) {
+        one_group[0] = 0;
+        one_group[1] = (int32_t)M;
+        off = one_group;
+        G = 1;
+    }
+    int64_t* P = (int64_t*)malloc(sizeof(int64_t) * (size_t)(G + 1));
+    P[0] = 0;
+    for (int32_t g = 0; g < G; ++g) {
+        int64_t mg = (int64_t)off[g + 1] - off[g];
+        P[g + 1] = P[g] + 256 * ((mg + 255) / 256);
+    }
+    if (P[G] > Mcap) {
+        free(P);
+        return -1;
+    }
+    memset(qT, 0, (size_t)(N * Mcap));
+    memset(sT, 0, (size_t)(N * (Mcap / 32)));
+    uint16_t col[32];
+    for (int32_t g = 0; g < G; ++g) {
+        int64_t r0 = off[g], r1 = off[g + 1];
+        for (int64_t n = 0; n < N; ++n) {
+            for (int64_t j = 0; r0 + 32 * j < r1; ++j) {
+                int64_t first = r0 + 32 * j;
+                int64_t cnt = r1 - first < 32 ? r1 - first : 32;
+                for (int64_t i = 0; i < cnt; ++i) col[i] = x[(first + i) * N + n];
+                /* the missing tail of the last block is zero padding: it adds
+                   nothing to amax and its codes stay 0x00 (set above) */
+                uint8_t S = mxref_block_scale(col, cnt, 1);
+                int64_t dst = P[g] + 32 * j;
+                sT[n * (Mcap / 32) + dst / 32] = S;
+                mxref_quantize_with_scale(col, cnt, S, qT + n * Mcap + dst);
+            }
+        }
+    }
+    if (padded)
+        for (int32_t g = 0; g <= G; ++g) padded[g] = (int32_t)P[g];
+    free(P);
+    return 0;
+}
+
+/*
+ * Packed scale order.  The gfx950 scaled matrix instruction
+ * v_mfma_scale_f32_32x32x64_f8f6f4 takes, per lane l (0..63), one 32-bit
+ * scale register and a byte selector: lane l scales row (l mod 32) of its
+ * 32-row operand for 32-wide K block (l div 32) of the 64-wide K step.  Four
+ * consecutive K steps (256 elements of K = 8 blocks) therefore share one
+ * register per lane, byte j serving step j.  The packed array is cut into
+ * units of 32 rows x 8 blocks = 256 bytes, each laid out as the 64 lane
+ * registers in lane order:
+ *     unit(r, b)  = (r div 32) * (KB * 32) + (b div 8) * 256
+ *     lane(r, b)  = 32 * (b mod 2) + (r mod 32)
+ *     byte(r, b)  = (b mod 8) div 2
+ *     offset      = unit + 4 * lane + byte
+ * with KB = 8 * ceil(K / 256) bytes per row and rows padded to a multiple
+ * of 32.  Pad bytes are zero.
+ */
+static int64_t packed_offset(int64_t r, int64_t b, int64_t KB) {
+    int64_t unit = (r / 32) * (KB * 32) + (b / 8) * 256;
+    int64_t lane = 32 * (b % 2) + (r % 32);
+    int64_t byte = (b % 8) / 2;
+    return unit + 4 * lane + byte;
+}
+
+int64_t mxref_packed_scale_bytes(int64_t R, int64_t K) {
+    int64_t KB = 8 * ((K + 255) / 256);
+    return ((R + 31) / 32) * 32 * KB;
+}
+
+void mxref_pack_scales(const uint8_t* s, int64_t R, int64_t K, uint8_t* packed) {
+    int64_t KB = 8 * ((K + 255) / 256);
+    int64_t nb = K / 32;
+    memset(packed, 0, (size_t)mxref_packed_scale_bytes(R, K));
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t b = 0; b < nb; ++b) packed[packed_offset(r, b, KB)] = s[r * nb + b];
+}
+
+void mxref_unpack_scales(const uint8_t* packed, int64_t R, int64_t K, uint8_t* s) {
+    int64_t KB = 8 * ((K + 255) / 256);
+    int64_t nb = K / 32;
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t b = 0; b < nb; ++b) s[r * nb + b] = packed[packed_offset(r, b, KB)];
+}
+
+/* One output element of the grouped GEMM: a plain fp64 dot product of the
+ * dequantized row of X and the dequantized row n of expert g's weights.
+ * Each product is exact in double (two 4-bit significands); the sum runs in
+ * order of k. */
+static double gemm_point(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
+                         int32_t g, int64_t m, int64_t n, int64_t N, int64_t K) {
+    int64_t nb = K / 32;
+    const uint8_t* xr = Xq + m * K;
+    const uint8_t* xs = Xs + m * nb;
+    const uint8_t* wr = Wq + ((int64_t)g * N + n) * K;
+    const uint8_t* ws = Ws + ((int64_t)g * N + n) * nb;
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k)
+        acc += mxref_dequant(xr[k], xs[k / 32]) * mxref_dequant(wr[k], ws[k / 32]);
+    return acc;
+}
+
+void mxref_grouped_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
+                        const int32_t* off, int32_t G, int64_t M, int64_t N, int64_t K, double* out) {
+    memset(out, 0, sizeof(double) * (size_t)(M * N));
+    for (int32_t g = 0; g < G; ++g)
+        for (int64_t m = off[g]; m < off[g + 1]; ++m)
+            for (int64_t n = 0; n < N; ++n) out[m * N + n] = gemm_point(Xq, Xs, Wq, Ws, g, m, n, N, K);
+}
+
+static int32_t group_of_row(const int32_t* off, int32_t G, int64_t m) {
+    for (int32_t g = 0; g < G; ++g)
+        if (m >= off[g] && m < off[g + 1]) return g;
+    return -1;
+}
+
+void mxref_grouped_gemm_points(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq,
+                               const uint8_t* Ws, const int32_t* off, int32_t G, int64_t M,
+                               int64_t N, int64_t K, const int64_t* rows, const int64_t* cols,
+                               int64_t npts, double* out) {
+    (void)M;
+    for (int64_t i = 0; i < npts; ++i) {
+        int32_t g = group_of_row(off, G, rows[i]);
+        out[i] = g < 0 ? 0.0 : gemm_point(Xq, Xs, Wq, Ws, g, rows[i], cols[i], N, K);
+    }
+}
+
+static double wgrad_point(const uint8_t* Aq, const uint8_t* As, const uint8_t* Bq, const uint8_t* Bs,
+                          const int32_t* P, int32_t g, int64_t n, int64_t k, int64_t Mcap) {
+    int64_t nb = Mcap / 32;
+    double acc = 0.0;
+    for (int64_t t = P[g]; t < P[g + 1]; ++t)
+        acc += mxref_dequant(Aq[n * Mcap + t], As[n * nb + t / 32]) *
+               mxref_dequant(Bq[k * Mcap + t], Bs[k * nb + t / 32]);
+    return acc;
+}
+
+void mxref_wgrad(const uint8_t* Aq, const uint8_t* As, const uint8_t* Bq, const uint8_t* Bs,
+                 const int32_t* P, int32_t G, int64_t N, int64_t K, int64_t Mcap, double* dW) {
+    for (int32_t g = 0; g < G; ++g)
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t k = 0; k < K; ++k)
+                dW[((int64_t)g * N + n) * K + k] = wgrad_point(Aq, As, Bq, Bs, P, g, n, k, Mcap);
+}
+
+void mxref_wgrad_points(const uint8_t* Aq, const uint8_t* As, const uint8_t* Bq, const uint8_t* Bs,
+                        const int32_t* P, int32_t G, int64_t N, int64_t K, int64_t Mcap,
+                        const int64_t* gs, const int64_t* ns, const int64_t* ks, int64_t npts,
+                        double* out) {
+    (void)G;
+    (void)N;
+    (void)K;
+    for (int64_t i = 0; i < npts; ++i) out[i] = wgrad_point(Aq, As, Bq, Bs, P, (int32_t)gs[i], ns[i], ks[i], Mcap);
+}
