@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP8 hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--seed S] [--no-gemm] [--no-cpu]
+
+Prints ONE JSON line.  The headline (``value``) is the quantize bandwidth on
+the quantize-only workload, bf16 [131072, 7168] ~ N(0,1) with 0.1 % of the
+elements scaled by 100: one step = one row-wise pass + one column-wise
+(transposed) pass, each writing fp8 codes and packed E8M0 scales.
+Throughput = algorithmic bytes (2 B read + 1 B + 1/32 B written per element,
+per pass; the byte count of the lpnh.cn 2479732 section 4 benchmark with bf16
+input) / GPU time, inputs resident in HBM.
+
+The ``gemm`` object times the grouped GEMMs on the MoE workloads (TFLOP/s =
+2 M N K over real rows / GPU time): gate+up (32768 x 7168 -> 4096, 16 experts),
+the ragged 128-expert case next to the dense GEMM of the same size, and the
+down projection forward / dgrad / wgrad.
+
+``roofline`` describes the dominant kernel of the step (its own launch time
+from HIP events on the launch stream); ``cpu_baseline`` times the CPU oracle
+on a bounded sample of the same workload (a reported baseline, not a target).
+"""
+import argparse
+import concurrent.futures
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_TBS = 8.0          # MI355X HBM3E, TB/s
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense MXFP8 MFMA, TFLOP/s
+METRIC = "MXFP8 quantize TB/s; grouped-GEMM TFLOP/s; each as % of HBM/MFMA peak"
+
+
+def quant_bytes(M, K):
+    return 2 * M * K + M * K + M * K // 32
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "mxfp8_block_scaled_04_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, digest):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 --pmc
+    summary (profiles/<kernel>_pmc.txt), if it was taken on this source."""
+    path = os.path.join(ROOT, "profiles", kernel + "_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != digest:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """HIP events on the stream the kernels are launched on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def run(self, fn, steps):
+        self.a.record()
+        for _ in range(steps):
+            fn()
+        self.b.record()
+        self.b.synchronize()
+        return self.a.elapsed_time(self.b) / steps  # ms per launch
+
+
+def cpu_baseline(x_cpu_rows, seed):
+    """Oracle (as it stands) on a bounded sample: rows then cols of the given
+    bf16 rows, split over host threads (ctypes releases the GIL)."""
+    import numpy as np
+    import oracle
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    bits = x_cpu_rows
+    M, K = bits.shape
+    chunks = np.array_split(np.arange(M), cores)
+    t0 = time.perf_counter()
+    with concurrent.futures.ThreadPoolExecutor(cores) as ex:
+        list(ex.map(lambda r: oracle.quantize_rows(bits[r[0]:r[-1] + 1]), chunks))
+    t_rows = time.perf_counter() - t0
+    # column-wise: blocks of 32 rows; 256-row slabs are independent
+    slabs = [np.arange(i, min(i + 256, M)) for i in range(0, M, 256)]
+    groups = np.array_split(np.arange(len(slabs)), cores)
+
+    def run_cols(gi):
+        for i in gi:
+            r = slabs[i]
+            oracle.quantize_cols(bits[r[0]:r[-1] + 1])
+
+    t0 = time.perf_counter()
+    with concurrent.futures.ThreadPoolExecutor(cores) as ex:
+        list(ex.map(run_cols, groups))
+    t_cols = time.perf_counter() - t0
+    tbs = 2 * quant_bytes(M, K) / (t_rows + t_cols) / 1e12
+    return {"value": tbs, "unit": "TB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{M} rows x {K} of the quantize workload (seed {seed}), row-wise then column-wise pass; "
+                      f"{t_rows:.2f} s + {t_cols:.2f} s wall"}
+
+
+def bench_quant(torch, mx, W, args):
+    x = W.quant_bandwidth(seed=args.seed, device="cuda")
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    s = torch.empty(mx.mx_scale_bytes(M, K), dtype=torch.uint8, device="cuda")
+    Mcap = mx.mx_cols_capacity(M, 1)
+    qT = torch.empty((K, Mcap), dtype=torch.uint8, device="cuda")
+    sT = torch.empty(mx.mx_scale_bytes(K, Mcap), dtype=torch.uint8, device="cuda")
+
+    def rows():
+        mx.mx_quantize_rows(x, q, s)
+
+    def cols():
+        mx.mx_quantize_cols(x, None, Mcap, qT, sT)
+
+    for _ in range(args.warmup):
+        rows()
+        cols()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    t0 = time.perf_counter()
+    ms_rows = tm.run(rows, args.steps)
+    ms_cols = tm.run(cols, args.steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    nbytes = quant_bytes(M, K)
+    res = {
+        "M": M, "K": K, "ms_rows": ms_rows, "ms_cols": ms_cols, "wall_s": wall,
+        "bytes_per_pass": nbytes,
+        "tbs_rows": nbytes / ms_rows / 1e9, "tbs_cols": nbytes / ms_cols / 1e9,
+    }
+    sample = None
+    if not args.no_cpu:
+        n = args.cpu_rows
+        sample = x[:n].cpu().contiguous().view(torch.int16).numpy().view("uint16")
+    del x, q, s, qT, sT
+    torch.cuda.empty_cache()
+    return res, sample
+
+
+def tflops(M, N, K, ms):
+    return 2.0 * M * N * K / (ms * 1e-3) / 1e12
+
+
+def bench_gemm(torch, mx, W, args):
+    out = {}
+    tm = Timer(torch)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        return tm.run(fn, args.steps)
+
+    # gate+up projection, 16 experts
+    d = W.moe_gate_up(seed=args.seed, device="cuda")
+    G, N, K = d["G"], d["N"], d["K"]
+    Xq, Xs = mx.mx_quantize_rows(d["x"])
+    Wq, Ws = mx.mx_quantize_rows(d["w"].reshape(G * N, K))
+    Wq = Wq.reshape(G, N, K)
+    off = torch.from_numpy(d["offsets"]).to("cuda")
+    y = torch.empty((d["M"], N), dtype=torch.bfloat16, device="cuda")
+    ms = timed(lambda: mx.mx_grouped_gemm(Xq, Xs, Wq, Ws, off, out=y))
+    qx = timed(lambda: mx.mx_quantize_rows(d["x"], Xq, Xs))
+    out["gate_up"] = {"M": d["M"], "N": N, "K": K, "G": G, "ms": ms, "tflops": tflops(d["M"], N, K, ms),
+                      "frac_mfma_peak": tflops(d["M"], N, K, ms) / MFMA_FP8_PEAK_TFLOPS,
+                      "quantize_x_ms": qx, "quantize_over_gemm": qx / ms}
+    del d, Xq, Xs, Wq, Ws, y
+    torch.cuda.empty_cache()
+
+    # ragged 128 experts vs dense
+    d = W.moe_ragged(seed=args.seed, device="cuda")
+    G, N, K, M = d["G"], d["N"], d["K"], d["M"]
+    Xq, Xs = mx.mx_quantize_rows(d["x"])
+    Wq, Ws = mx.mx_quantize_rows(d["w"].reshape(G * N, K))
+    Wq = Wq.reshape(G, N, K)
+    Dq, Ds = mx.mx_quantize_rows(d["w_dense"].reshape(N, K))
+    Dq = Dq.reshape(1, N, K)
+    off = torch.from_numpy(d["offsets"]).to("cuda")
+    off1 = torch.tensor([0, M], dtype=torch.int32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ms_g = timed(lambda: mx.mx_grouped_gemm(Xq, Xs, Wq, Ws, off, out=y))
+    ms_d = timed(lambda: mx.mx_grouped_gemm(Xq, Xs, Dq, Ds, off1, out=y))
+    out["ragged"] = {"M": M, "N": N, "K": K, "G": G, "ms_grouped": ms_g, "ms_dense": ms_d,
+                     "tflops_grouped": tflops(M, N, K, ms_g), "tflops_dense": tflops(M, N, K, ms_d),
+                     "grouped_over_dense": ms_g / ms_d,
+                     "frac_mfma_peak_grouped": tflops(M, N, K, ms_g) / MFMA_FP8_PEAK_TFLOPS}
+    del d, Xq, Xs, Wq, Ws, Dq, Ds, y
+    torch.cuda.empty_cache()
+
+    # down projection forward / dgrad / wgrad
+    d = W.moe_down_backward(seed=args.seed, device="cuda")
+    G, N, K, M = d["G"], d["N"], d["K"], d["M"]
+    off = torch.from_numpy(d["offsets"]).to("cuda")
+    Xq, Xs = mx.mx_quantize_rows(d["x"])
+    Wq, Ws = mx.mx_quantize_rows(d["w"].reshape(G * N, K))
+    Wq = Wq.reshape(G, N, K)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ms_f = timed(lambda: mx.mx_grouped_gemm(Xq, Xs, Wq, Ws, off, out=y))
+    dyq, dys = mx.mx_quantize_rows(d["dy"])
+    woff = torch.arange(0, G + 1, dtype=torch.int32, device="cuda") * N
+    wT, wTs, _ = mx.mx_quantize_cols(d["w"].reshape(G * N, K), woff)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    ms_dg = timed(lambda: mx.mx_grouped_gemm_dgrad(dyq, dys, wT, wTs, off, G, out=dx))
+    A, As, P = mx.mx_quantize_cols(d["dy"], off)
+    B, Bs, _ = mx.mx_quantize_cols(d["x"], off)
+    dW = torch.empty((G, N, K), dtype=torch.bfloat16, device="cuda")
+    ms_wg = timed(lambda: mx.mx_grouped_gemm_wgrad(A, As, B, Bs, P, dW=dW))
+    ms_qc = timed(lambda: mx.mx_quantize_cols(d["dy"], off, A.shape[1], A, As, P))
+    out["down_backward"] = {
+        "M": M, "N": N, "K": K, "G": G,
+        "ms_fwd": ms_f, "tflops_fwd": tflops(M, N, K, ms_f),
+        "ms_dgrad": ms_dg, "tflops_dgrad": tflops(M, K, N, ms_dg),
+        "ms_wgrad": ms_wg, "tflops_wgrad": tflops(N, K, M, ms_wg),
+        "quantize_cols_dy_ms": ms_qc,
+    }
+    del d
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-gemm", action="store_true", help="skip the grouped-GEMM section")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=16384, help="rows of the oracle sample")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU layout is described in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mxfp8_block_scaled_04_amd as mx
+    from mxfp8_block_scaled_04_amd import workloads as W
+
+    mx.load()
+    torch.cuda.set_device(0)
+    quant, sample = bench_quant(torch, mx, W, args)
+    gemm = None if args.no_gemm else bench_gemm(torch, mx, W, args)
+    cpu = None if sample is None else cpu_baseline(sample, args.seed)
+
+    ms_step = quant["ms_rows"] + quant["ms_cols"]
+    value = 2 * quant["bytes_per_pass"] / (ms_step * 1e-3) / 1e12
+    dominant = "quantize_cols_kernel" if quant["ms_cols"] >= quant["ms_rows"] else "quantize_rows_kernel"
+    dom_ms = max(quant["ms_rows"], quant["ms_cols"])
+    achieved = quant["bytes_per_pass"] / (dom_ms * 1e-3) / 1e9  # GB/s
+    digest = source_digest("quantize.hip", "mx_device.h")
+    traffic = load_traffic(dominant, digest)
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16->fp8_e4m3+e8m0",
+        "data": "synthetic (seeded N(0,1) bf16, 0.1% outliers x100)",
+        "config": {"workload": "quantize_bandwidth bf16 [131072, 7168], row-wise + column-wise pass",
+                   "seed": args.seed, "frac_hbm_peak": value / HBM_PEAK_TBS,
+                   "tbs_rows": quant["tbs_rows"], "tbs_cols": quant["tbs_cols"],
+                   "ms_rows": quant["ms_rows"], "ms_cols": quant["ms_cols"],
+                   "source_sha256": digest},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_TBS * 1000,
+                     "unit": "GB/s", "frac": achieved / (HBM_PEAK_TBS * 1000), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": quant["bytes_per_pass"]},
+        "cpu_baseline": cpu,
+        "gemm": gemm,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

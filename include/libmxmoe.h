@@ -1,0 +1,170 @@
+/*
+ * libmxmoe -- MXFP8 quantization and block-scaled grouped GEMM for AMD
+ * Instinct MI355X (gfx950).  C ABI.
+ *
+ * What it computes follows the public write-ups on Cursor's Blackwell MoE
+ * kernels:
+ *  - lpnh.cn 2479732, section 1: MX block scaling -- cut the tensor into
+ *    blocks of 32 elements, compute one scale per block, divide the block by
+ *    it and cast to FP8 E4M3; the forward pass quantizes its input matrix
+ *    and writes it back to memory, the backward pass needs a transposed
+ *    quantization as well.
+ *  - aigc.bar "被忽视的量化税" / "秘密武器": the quantization kernel writes its
+ *    scales in the layout the matrix instruction consumes, so no reshape pass
+ *    sits between quantization and the GEMM; FP8 E4M3 with block size 32.
+ *  - aigc.bar "为MoE量身定制优化": the per-expert grouped GEMM, scheduled with
+ *    expert-aware cache reuse.
+ * Readings of what the pages leave open (fixed here, identical in every
+ * entry point):
+ *  - scale byte S is E8M0 (value 2^(S-127)); S = clamp(floor(log2 amax) - 8,
+ *    -127, 127) + 127, and S = 0 for an all-zero block;
+ *  - element code = OCP E4M3FN of x * 2^(127-S), saturated to +/-448, round to
+ *    nearest even, sign kept for zero; bf16 subnormals are exact inputs;
+ *  - inputs are finite (non-finite inputs give unspecified codes).
+ *
+ * Data formats
+ *  - bf16 tensors are arrays of uint16 bit patterns, row-major.
+ *  - FP8 codes are one byte per element, row-major, same shape as the input
+ *    (column-wise results are stored transposed, see mx_quantize_cols).
+ *  - Scales are stored in the PACKED order of the gfx950 instruction
+ *    v_mfma_scale_f32_32x32x64_f8f6f4, for a matrix of R rows and a
+ *    contraction length K (K % 32 == 0):
+ *        KB     = 8 * ceil(K / 256)                 bytes per row
+ *        size   = ceil(R / 32) * 32 * KB            bytes (mx_scale_bytes)
+ *        offset(r, b) = (r / 32) * 32 * KB + (b / 8) * 256
+ *                       + 4 * (32 * (b % 2) + r % 32) + (b % 8) / 2
+ *    for row r and 32-wide block b.  Each 256-byte unit is the 64 lane
+ *    registers of one 32-row x 256-K slice in lane order; byte j of a lane
+ *    register serves the j-th 64-wide K step.  Pad bytes are written as 0.
+ *
+ * Conventions
+ *  - Every pointer argument is a DEVICE pointer owned by the caller.  The
+ *    library allocates nothing, keeps no state, never synchronizes and never
+ *    reads device data on the host.  Every call is asynchronous on `stream`
+ *    (a hipStream_t; NULL = the default stream).
+ *  - Host-checkable preconditions are validated before any launch; a
+ *    failing call returns an error code and launches nothing.  A launch
+ *    failure returns MX_ERR_HIP.
+ *  - group_offsets is an int32 device array of G+1 exclusive prefix
+ *    offsets: [0] = 0, non-decreasing, [G] = M; empty groups are allowed.
+ *    Entries are clamped on the device to stay monotone within [0, M], so a
+ *    malformed array gives wrong results but no out-of-bounds access.
+ *  - M = 0 (and empty groups) are legal and do no work.
+ */
+#ifndef LIBMXMOE_H
+#define LIBMXMOE_H
+#include <stdint.h>
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MX_OK = 0,
+    MX_ERR_NULL = 1,        /* a required pointer is NULL */
+    MX_ERR_SHAPE = 2,       /* negative size, K % 32 != 0, ld too small, ... */
+    MX_ERR_ALIGN = 3,       /* a pointer or leading dimension is not 16-byte aligned */
+    MX_ERR_CAPACITY = 4,    /* Mcap below mx_cols_capacity(M, G) or not a multiple of 256 */
+    MX_ERR_UNSUPPORTED = 5, /* valid per the format but not supported by these kernels */
+    MX_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+} mx_status;
+
+/* Short human-readable name of a status code (static string). */
+const char* mx_status_str(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int mx_version(void);
+
+/* Bytes of the packed scale array for R rows and contraction length K. */
+int64_t mx_scale_bytes(int64_t R, int64_t K);
+
+/* Upper bound of the padded column count of mx_quantize_cols for M rows in
+ * G groups: 256 * (ceil(M / 256) + G - 1) (G = 1 when offsets are NULL). */
+int64_t mx_cols_capacity(int64_t M, int32_t G);
+
+/*
+ * Row-wise MXFP8 quantization (scales along K; the forward-pass operand
+ * layout -- lpnh.cn 2479732 section 1).
+ *   x   bf16 [M][ldx] (first K columns used), 16-byte aligned, ldx % 8 == 0
+ *   q   uint8 [M][K] codes, 16-byte aligned
+ *   s   packed scales for R = M rows, contraction K (mx_scale_bytes(M, K))
+ * Requires K % 32 == 0, ldx >= K.
+ */
+mx_status mx_quantize_rows(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                           uint8_t* s, void* stream);
+
+/*
+ * Column-wise (transposed) MXFP8 quantization: blocks of 32 consecutive rows
+ * of one column (the backward-pass transpose-quantize -- lpnh.cn 2479732
+ * section 1).  Rows are split into groups by group_offsets (NULL = one
+ * group of all M rows, G ignored); blocks restart at each group's first row
+ * and the group's tail is zero-padded to a multiple of 256 rows.  Group g
+ * lands at padded column P[g] = sum_{h<g} 256 * ceil(m_h / 256) of the
+ * transposed result.
+ *   x        bf16 [M][ldx] (first N columns used), 16-byte aligned, ldx % 8 == 0
+ *   qT       uint8 [N][Mcap] codes (row n = column n of x); columns >= P[G] are 0
+ *   sT       packed scales for R = N rows, contraction Mcap (mx_scale_bytes(N, Mcap))
+ *   padded_offsets  int32 [G+1] device output P (required when group_offsets
+ *            is given; may be NULL otherwise)
+ * Requires N % 8 == 0, Mcap % 256 == 0, Mcap >= mx_cols_capacity(M, G),
+ * 1 <= G <= 4096.
+ */
+mx_status mx_quantize_cols(const uint16_t* x, int64_t M, int64_t N, int64_t ldx,
+                           const int32_t* group_offsets, int32_t G, uint8_t* qT, uint8_t* sT,
+                           int64_t Mcap, int32_t* padded_offsets, void* stream);
+
+/*
+ * Grouped GEMM (M-grouped; forward and dgrad): rows [o_g, o_{g+1}) of X use
+ * expert g's weights (aigc.bar "为MoE量身定制优化"; lpnh.cn 2479732 section 1):
+ *   out[m][n] = sum_k deq(Xq[m][k]) * deq(Wq[g][n][k]),   fp32 accumulation,
+ * scales applied by the matrix instruction per 32-wide K block, result
+ * rounded to bf16 (nearest even).  Every output row in [0, M) that belongs
+ * to a group is written exactly once.
+ *   Xq  uint8 [M][K], Xs packed scales (R = M, contraction K)
+ *   Wq  uint8 [G][N][K], Ws packed scales of the [G*N][K] matrix
+ *   out bf16 [M][N]
+ * Requires K % 256 == 0 (MX_ERR_UNSUPPORTED otherwise), 1 <= G <= 4096,
+ * 16-byte aligned pointers.  G = 1 with offsets {0, M} is a dense GEMM.
+ */
+mx_status mx_grouped_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq,
+                          const uint8_t* Ws, const int32_t* group_offsets, int32_t G, int64_t M,
+                          int64_t N, int64_t K, uint16_t* out, void* stream);
+
+/*
+ * Data-gradient grouped GEMM (M-grouped, weights read transposed; the
+ * backward pass of lpnh.cn 2479732 section 1):
+ *   dX[m][n] = sum_k deq(dY[m][k]) * deq(W[g(m)][k][n])
+ * with W^T taken straight from mx_quantize_cols of the weights viewed as
+ * [G*K][N] with group offsets {0, K, 2K, ..., GK}: that call stores expert
+ * g's W^T as the column slice [g K, g K + K) of WT [N][Wcap], which this call
+ * reads in place (no re-layout).  Here K is the forward output width (the
+ * contraction of dgrad) and N the forward input width.
+ *   dYq uint8 [M][K], dYs packed scales (R = M, contraction K)
+ *   WTq uint8 [N][Wcap], WTs packed scales (R = N, contraction Wcap)
+ *   dX  bf16 [M][N]
+ * Requires K % 256 == 0 (so that expert g starts at column g K), Wcap %
+ * 256 == 0, Wcap >= G * K, 1 <= G <= 4096.
+ */
+mx_status mx_grouped_gemm_dgrad(const uint8_t* dYq, const uint8_t* dYs, const uint8_t* WTq,
+                                const uint8_t* WTs, const int32_t* group_offsets, int32_t G,
+                                int64_t M, int64_t N, int64_t K, int64_t Wcap, uint16_t* dX,
+                                void* stream);
+
+/*
+ * Weight-gradient grouped GEMM (contraction-grouped): groups partition the
+ * contraction axis by the padded offsets P written by mx_quantize_cols
+ * (lpnh.cn 2479732 section 1, the backward pass):
+ *   dW[g][n][k] = sum_{t in [P[g], P[g+1])} deq(A[n][t]) * deq(B[k][t])
+ *   A   uint8 [N][Mcap] (dY^T, column-wise quantized), As packed (R = N, Mcap)
+ *   B   uint8 [K][Mcap] (X^T, column-wise quantized),  Bs packed (R = K, Mcap)
+ *   dW  bf16 [G][N][K]; an empty group gets an all-zero dW[g]
+ * Requires Mcap % 256 == 0, 1 <= G <= 4096.  P entries are rounded down to
+ * multiples of 256 and clamped to [0, Mcap] on the device.
+ */
+mx_status mx_grouped_gemm_wgrad(const uint8_t* A, const uint8_t* As, const uint8_t* B,
+                                const uint8_t* Bs, const int32_t* padded_offsets, int32_t G,
+                                int64_t N, int64_t K, int64_t Mcap, uint16_t* dW, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBMXMOE_H */

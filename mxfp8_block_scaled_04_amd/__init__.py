@@ -1,0 +1,176 @@
+"""Python binding of libmxmoe (MXFP8 quantization + block-scaled grouped GEMM
+for MI355X / gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of
+``libmxmoe.so``; PyTorch supplies device memory and the stream.  The
+functions carry the names of the C entry points (see include/libmxmoe.h for
+the contract of each).  If the library has not been built, importing works
+but every call raises ``RuntimeError`` -- there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxmoe.so")
+
+MX_OK = 0
+_lib = None
+
+
+class MxError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} ({status})")
+
+
+def load():
+    """Load libmxmoe.so (built by ``python -m mxfp8_block_scaled_04_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libmxmoe.so not built ({LIB_PATH}); run python -m mxfp8_block_scaled_04_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, ST = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+    lib.mx_status_str.argtypes = [ctypes.c_int]
+    lib.mx_status_str.restype = ctypes.c_char_p
+    lib.mx_version.restype = ctypes.c_int
+    lib.mx_scale_bytes.argtypes = [I64, I64]
+    lib.mx_scale_bytes.restype = I64
+    lib.mx_cols_capacity.argtypes = [I64, I32]
+    lib.mx_cols_capacity.restype = I64
+    lib.mx_quantize_rows.argtypes = [P, I64, I64, I64, P, P, P]
+    lib.mx_quantize_rows.restype = ST
+    lib.mx_quantize_cols.argtypes = [P, I64, I64, I64, P, I32, P, P, I64, P, P]
+    lib.mx_quantize_cols.restype = ST
+    lib.mx_grouped_gemm.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, P]
+    lib.mx_grouped_gemm.restype = ST
+    lib.mx_grouped_gemm_dgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, I64, P, P]
+    lib.mx_grouped_gemm_dgrad.restype = ST
+    lib.mx_grouped_gemm_wgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, P]
+    lib.mx_grouped_gemm_wgrad.restype = ST
+    _lib = lib
+    return lib
+
+
+# Exported C symbols, in header order.
+SYMBOLS = (
+    "mx_status_str", "mx_version", "mx_scale_bytes", "mx_cols_capacity", "mx_quantize_rows",
+    "mx_quantize_cols", "mx_grouped_gemm", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad",
+)
+
+
+def status_str(status):
+    try:
+        return load().mx_status_str(int(status)).decode()
+    except RuntimeError:
+        return str(status)
+
+
+def mx_scale_bytes(R, K):
+    return int(load().mx_scale_bytes(int(R), int(K)))
+
+
+def mx_cols_capacity(M, G=1):
+    return int(load().mx_cols_capacity(int(M), int(G)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(rc, where):
+    if rc != MX_OK:
+        raise MxError(rc, where)
+
+
+def _bits16(x):
+    if x.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return x
+    raise TypeError(f"expected bf16 (or its 16-bit pattern), got {x.dtype}")
+
+
+def mx_quantize_rows(x, q=None, s=None, stream=None):
+    """Row-wise MXFP8 of bf16 x [M, K] (row stride may exceed K).
+    Returns (q uint8 [M, K], s uint8 packed scales [mx_scale_bytes(M, K)])."""
+    x = _bits16(x)
+    M, K = x.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty(mx_scale_bytes(M, K), dtype=torch.uint8, device=x.device)
+    rc = load().mx_quantize_rows(_ptr(x), M, K, x.stride(0), _ptr(q), _ptr(s), _stream(stream))
+    _check(rc, "mx_quantize_rows")
+    return q, s
+
+
+def mx_quantize_cols(x, group_offsets=None, Mcap=None, qT=None, sT=None, padded_offsets=None, stream=None):
+    """Column-wise (transposed) MXFP8 of bf16 x [M, N] with optional row groups.
+    Returns (qT uint8 [N, Mcap], sT packed scales, padded_offsets int32 [G+1] or None)."""
+    x = _bits16(x)
+    M, N = x.shape
+    G = 1 if group_offsets is None else group_offsets.numel() - 1
+    if Mcap is None:
+        Mcap = mx_cols_capacity(M, G)
+    if qT is None:
+        qT = torch.empty((N, Mcap), dtype=torch.uint8, device=x.device)
+    if sT is None:
+        sT = torch.empty(mx_scale_bytes(N, Mcap), dtype=torch.uint8, device=x.device)
+    if group_offsets is not None and padded_offsets is None:
+        padded_offsets = torch.empty(G + 1, dtype=torch.int32, device=x.device)
+    rc = load().mx_quantize_cols(_ptr(x), M, N, x.stride(0), _ptr(group_offsets), G, _ptr(qT), _ptr(sT), Mcap,
+                                 _ptr(padded_offsets), _stream(stream))
+    _check(rc, "mx_quantize_cols")
+    return qT, sT, padded_offsets
+
+
+def mx_grouped_gemm(Xq, Xs, Wq, Ws, group_offsets, out=None, stream=None):
+    """out[m, n] = sum_k deq(Xq[m, k]) deq(Wq[g(m), n, k]) in bf16.
+    Xq uint8 [M, K]; Wq uint8 [G, N, K]; scales packed; group_offsets int32 [G+1]."""
+    M, K = Xq.shape
+    G, N, K2 = Wq.shape
+    if K2 != K:
+        raise ValueError("K mismatch")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=Xq.device)
+    rc = load().mx_grouped_gemm(_ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), _ptr(group_offsets), G, M, N, K, _ptr(out),
+                                _stream(stream))
+    _check(rc, "mx_grouped_gemm")
+    return out
+
+
+def mx_grouped_gemm_dgrad(dYq, dYs, WTq, WTs, group_offsets, G, out=None, stream=None):
+    """dX[m, n] = sum_k deq(dY[m, k]) deq(W[g(m), k, n]) in bf16, with W^T read in
+    place from mx_quantize_cols of W.view(G*K, N) (offsets g*K): WTq [N, Wcap]."""
+    M, K = dYq.shape
+    N, Wcap = WTq.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dYq.device)
+    rc = load().mx_grouped_gemm_dgrad(_ptr(dYq), _ptr(dYs), _ptr(WTq), _ptr(WTs), _ptr(group_offsets), int(G), M, N,
+                                      K, Wcap, _ptr(out), _stream(stream))
+    _check(rc, "mx_grouped_gemm_dgrad")
+    return out
+
+
+def mx_grouped_gemm_wgrad(A, As, B, Bs, padded_offsets, dW=None, stream=None):
+    """dW[g, n, k] = sum over group g's padded span of deq(A[n, t]) deq(B[k, t]).
+    A uint8 [N, Mcap] (dY^T), B uint8 [K, Mcap] (X^T); padded_offsets int32 [G+1]."""
+    N, Mcap = A.shape
+    K, Mcap2 = B.shape
+    if Mcap2 != Mcap:
+        raise ValueError("Mcap mismatch")
+    G = padded_offsets.numel() - 1
+    if dW is None:
+        dW = torch.empty((G, N, K), dtype=torch.bfloat16, device=A.device)
+    rc = load().mx_grouped_gemm_wgrad(_ptr(A), _ptr(As), _ptr(B), _ptr(Bs), _ptr(padded_offsets), G, N, K, Mcap,
+                                      _ptr(dW), _stream(stream))
+    _check(rc, "mx_grouped_gemm_wgrad")
+    return dW

@@ -1,0 +1,134 @@
+// C-ABI entry points of libmxmoe: argument validation, then the launchers.
+// See include/libmxmoe.h for the contract of each call.
+#include "../../include/libmxmoe.h"
+
+#include <hip/hip_runtime.h>
+
+#include "mx_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
+
+constexpr int32_t kMaxGroups = 4096;
+
+}  // namespace
+
+extern "C" {
+
+const char* mx_status_str(int status) {
+    switch (status) {
+        case MX_OK: return "MX_OK";
+        case MX_ERR_NULL: return "MX_ERR_NULL";
+        case MX_ERR_SHAPE: return "MX_ERR_SHAPE";
+        case MX_ERR_ALIGN: return "MX_ERR_ALIGN";
+        case MX_ERR_CAPACITY: return "MX_ERR_CAPACITY";
+        case MX_ERR_UNSUPPORTED: return "MX_ERR_UNSUPPORTED";
+        case MX_ERR_HIP: return "MX_ERR_HIP";
+        default: return "MX_ERR_UNKNOWN";
+    }
+}
+
+int mx_version(void) { return 100; }
+
+int64_t mx_scale_bytes(int64_t R, int64_t K) {
+    if (R < 0 || K < 0) return -1;
+    return ((R + 31) / 32) * 32 * (8 * ((K + 255) / 256));
+}
+
+int64_t mx_cols_capacity(int64_t M, int32_t G) {
+    if (M < 0 || G < 1) return -1;
+    return 256 * ((M + 255) / 256 + (int64_t)G - 1);
+}
+
+mx_status mx_quantize_rows(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, uint8_t* s,
+                           void* stream) {
+    if (M < 0 || K < 0 || K % 32 != 0 || ldx < K) return MX_ERR_SHAPE;
+    if (M == 0 || K == 0) return MX_OK;
+    if (!x || !q || !s) return MX_ERR_NULL;
+    if (!aligned16(x) || !aligned16(q) || !aligned16(s) || ldx % 8 != 0) return MX_ERR_ALIGN;
+    // one 256-thread workgroup per 32 x 256 unit; total work-items < 2^32
+    if (((M + 31) / 32) * ((K + 255) / 256) > (int64_t)(UINT32_MAX / 256)) return MX_ERR_UNSUPPORTED;
+    return from_hip(mx::launch_quantize_rows(x, M, K, ldx, q, s, (hipStream_t)stream));
+}
+
+mx_status mx_quantize_cols(const uint16_t* x, int64_t M, int64_t N, int64_t ldx, const int32_t* group_offsets,
+                           int32_t G, uint8_t* qT, uint8_t* sT, int64_t Mcap, int32_t* padded_offsets,
+                           void* stream) {
+    if (group_offsets == nullptr) G = 1;
+    if (M < 0 || N < 0 || ldx < N || Mcap < 0) return MX_ERR_SHAPE;
+    if (G < 1 || G > kMaxGroups) return MX_ERR_SHAPE;
+    if (N % 8 != 0) return MX_ERR_UNSUPPORTED;
+    if (Mcap % 256 != 0 || Mcap < mx_cols_capacity(M, G)) return MX_ERR_CAPACITY;
+    if (group_offsets != nullptr && padded_offsets == nullptr) return MX_ERR_NULL;
+    if (N == 0 || Mcap == 0) {
+        if (group_offsets == nullptr) return MX_OK;
+    } else {
+        if (!x && M > 0) return MX_ERR_NULL;
+        if (!qT || !sT) return MX_ERR_NULL;
+        if ((x && !aligned16(x)) || !aligned16(qT) || !aligned16(sT) || ldx % 8 != 0) return MX_ERR_ALIGN;
+    }
+    if (Mcap / 256 > (int64_t)UINT32_MAX / 256 || (N + 63) / 64 > 65535) return MX_ERR_UNSUPPORTED;  // grid
+    return from_hip(mx::launch_quantize_cols(x, M, N, ldx, group_offsets, G, qT, sT, Mcap, padded_offsets,
+                                             (hipStream_t)stream));
+}
+
+mx_status mx_grouped_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
+                          const int32_t* group_offsets, int32_t G, int64_t M, int64_t N, int64_t K, uint16_t* out,
+                          void* stream) {
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return MX_ERR_SHAPE;
+    if (G < 1 || G > kMaxGroups) return MX_ERR_SHAPE;
+    if (K % 256 != 0) return MX_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return MX_OK;
+    if (!Xq || !Xs || !Wq || !Ws || !group_offsets || !out) return MX_ERR_NULL;
+    if (!aligned16(Xq) || !aligned16(Xs) || !aligned16(Wq) || !aligned16(Ws) || !aligned16(out))
+        return MX_ERR_ALIGN;
+    // 32-bit per-tile offsets inside the kernel: 256 rows of an operand and
+    // 256 rows of the output must span < 4 GiB.
+    if (K > (1 << 23) || N > (1 << 22)) return MX_ERR_UNSUPPORTED;
+    // 32-bit scale offsets: packed scale arrays below 4 GiB
+    if (mx_scale_bytes(M, K) >= ((int64_t)1 << 32) || mx_scale_bytes((int64_t)G * N, K) >= ((int64_t)1 << 32))
+        return MX_ERR_UNSUPPORTED;
+    return from_hip(mx::launch_grouped_gemm(Xq, Xs, Wq, Ws, group_offsets, G, M, N, K, out, (hipStream_t)stream));
+}
+
+mx_status mx_grouped_gemm_dgrad(const uint8_t* dYq, const uint8_t* dYs, const uint8_t* WTq, const uint8_t* WTs,
+                                const int32_t* group_offsets, int32_t G, int64_t M, int64_t N, int64_t K,
+                                int64_t Wcap, uint16_t* dX, void* stream) {
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || Wcap < 0) return MX_ERR_SHAPE;
+    if (G < 1 || G > kMaxGroups) return MX_ERR_SHAPE;
+    if (K % 256 != 0) return MX_ERR_UNSUPPORTED;
+    if (Wcap % 256 != 0 || Wcap < (int64_t)G * K) return MX_ERR_CAPACITY;
+    if (M == 0 || N == 0) return MX_OK;
+    if (!dYq || !dYs || !WTq || !WTs || !group_offsets || !dX) return MX_ERR_NULL;
+    if (!aligned16(dYq) || !aligned16(dYs) || !aligned16(WTq) || !aligned16(WTs) || !aligned16(dX))
+        return MX_ERR_ALIGN;
+    if (K > (1 << 23) || N > (1 << 22) || Wcap > (1 << 23)) return MX_ERR_UNSUPPORTED;
+    if (mx_scale_bytes(M, K) >= ((int64_t)1 << 32) || mx_scale_bytes(N, Wcap) >= ((int64_t)1 << 32))
+        return MX_ERR_UNSUPPORTED;
+    return from_hip(mx::launch_grouped_gemm_dgrad(dYq, dYs, WTq, WTs, group_offsets, G, M, N, K, Wcap, dX,
+                                                  (hipStream_t)stream));
+}
+
+mx_status mx_grouped_gemm_wgrad(const uint8_t* A, const uint8_t* As, const uint8_t* B, const uint8_t* Bs,
+                                const int32_t* padded_offsets, int32_t G, int64_t N, int64_t K, int64_t Mcap,
+                                uint16_t* dW, void* stream) {
+    if (N < 0 || K < 0 || Mcap < 0) return MX_ERR_SHAPE;
+    if (G < 1 || G > kMaxGroups) return MX_ERR_SHAPE;
+    if (Mcap % 256 != 0) return MX_ERR_CAPACITY;
+    if (N == 0 || K == 0) return MX_OK;
+    if (!dW || !padded_offsets) return MX_ERR_NULL;
+    if (Mcap > 0 && (!A || !As || !B || !Bs)) return MX_ERR_NULL;
+    if ((A && !aligned16(A)) || (As && !aligned16(As)) || (B && !aligned16(B)) || (Bs && !aligned16(Bs)) ||
+        !aligned16(dW))
+        return MX_ERR_ALIGN;
+    if (Mcap > (1 << 23) || K > (1 << 22)) return MX_ERR_UNSUPPORTED;
+    if (mx_scale_bytes(N, Mcap) >= ((int64_t)1 << 32) || mx_scale_bytes(K, Mcap) >= ((int64_t)1 << 32))
+        return MX_ERR_UNSUPPORTED;
+    return from_hip(mx::launch_grouped_gemm_wgrad(A, As, B, Bs, padded_offsets, G, N, K, Mcap, dW,
+                                                  (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,525 @@
+// Block-scaled grouped GEMM for gfx950 (MXFP8 operands, fp32 accumulation,
+// bf16 output).
+//
+// Method (aigc.bar "为MoE量身定制优化" and "拥抱原生硬件指令"; lpnh.cn 2479732
+// section 5): per-expert GEMMs over variable row groups, with the block
+// scales applied by the matrix instruction itself (no dequantization pass),
+// and an expert-aware tile order so an expert's weights are reused from
+// cache.  On gfx950 the instruction is v_mfma_scale_f32_32x32x64_f8f6f4,
+// which takes one E8M0 byte per lane per operand; the packed scale layout
+// written by the quantize kernels hands each lane that byte for four
+// consecutive 64-wide K steps in one dword (byte = op_sel).
+//
+// Kernel: persistent workgroups of 4 waves, tile 256 x 256, K stage 128.
+//  * fp8 A/B stages go straight from global memory into LDS with 16-byte
+//    global_load_lds (no VGPR staging), two buffers, one stage in flight
+//    while the previous one is multiplied.  Rows are stored 128 bytes apart
+//    with the 16-byte granule index XORed by (row mod 8), so the fragment
+//    reads (32 rows, same K offset) hit distinct banks.
+//  * Each wave owns a 128 x 128 sub-tile = 4 x 4 MFMA blocks; per 64-wide K
+//    step a lane holds 16 bytes of each 32-wide block for its row.
+//  * Scale dwords come straight from global memory into VGPRs, one chunk
+//    (256 of K) ahead.
+//  * Tile order: expert-major; inside an expert, bands of 4 M-tiles walked
+//    M-fastest; workgroups are mapped so that each XCD (workgroups are
+//    dealt to the 8 XCDs round-robin) runs a contiguous range of tile ids
+//    and so shares operands through its own L2.
+#include "mx_device.h"
+#include "mx_internal.h"
+
+namespace mx {
+
+namespace {
+
+constexpr int TM = 256;
+constexpr int TN = 256;
+constexpr int TK = 128;
+constexpr int kBand = 4;  // M-tiles per band of the tile order
+
+typedef __attribute__((address_space(3))) void lds_t;
+typedef __attribute__((address_space(1))) void gbl_t;
+
+struct GemmArgs {
+    const uint8_t* A;
+    const uint8_t* As;
+    const uint8_t* B;
+    const uint8_t* Bs;
+    const int32_t* offsets;
+    uint16_t* out;
+    int64_t M, N, K, Mcap;
+    int32_t G;
+    int32_t mode;  // 0: rows of X grouped (forward); 1: contraction grouped (wgrad);
+                   // 2: rows grouped, weights read transposed (dgrad)
+    int64_t ldb;   // mode 2: row stride of the transposed weights (their Mcap)
+};
+
+struct Tile {
+    const uint8_t* A;   // base of A data (row 0)
+    const uint8_t* As;  // base of A packed scales (row 0)
+    int64_t lda, a_unit;  // row stride of A data; bytes per 32-row scale unit (32 * KB)
+    int64_t a_row0, a_lim;
+    const uint8_t* B;
+    const uint8_t* Bs;
+    int64_t ldb, b_unit;
+    int64_t b_row0, b_lim;
+    int64_t k0, k1;  // contraction range, multiples of 256
+    uint16_t* out;   // element (0, 0) of the tile
+    int64_t ldo;
+    int32_t rows, cols;  // valid part of the tile
+};
+
+__shared__ __attribute__((aligned(16))) uint8_t lds_a0[TM * TK];
+__shared__ __attribute__((aligned(16))) uint8_t lds_a1[TM * TK];
+__shared__ __attribute__((aligned(16))) uint8_t lds_b0[TN * TK];
+__shared__ __attribute__((aligned(16))) uint8_t lds_b1[TN * TK];
+__shared__ int32_t tile_end[kMaxGroups];  // inclusive prefix of tiles per group
+
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
+    return v < lo ? lo : (v > hi ? hi : v);
+}
+
+// 16-byte direct global->LDS load (global_load_lds_dwordx4): lane i of the
+// wave writes LDS bytes [lds + 16 i, lds + 16 i + 16).  Issued as inline asm
+// so that the compiler's own wait insertion does not stall every later LDS
+// read on it; completion is enforced explicitly (wait_vmem_all + barrier)
+// before the buffer is read.
+// The address base must be wave-uniform (an SGPR pair).
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// M0 is only written here; no other code in these kernels reads it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Pin the accumulators at this point of the program: the matrix ops that
+// produce them cannot be moved past it (in particular not past the next
+// barrier, which would leave that wait without work to hide it).
+__device__ __forceinline__ void pin_acc(f32x16 (&acc)[4][4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) asm volatile("" ::"a"(acc[i][j]));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) { return (uint32_t)(uintptr_t)(lds_t*)p; }
+
+// Issue the direct-to-LDS loads of one K stage: this wave's 64 rows of A and
+// of B (8 instructions each, 8 rows x 128 bytes per instruction).  abase and
+// bbase are the (uniform) addresses of the tile's first rows at column k.
+__device__ __forceinline__ void issue_stage(const uint8_t* abase, const uint8_t* bbase, const uint32_t (&aoffs)[8],
+                                            const uint32_t (&boffs)[8], uint8_t* la, uint8_t* lb, int w) {
+    const uint32_t a0 = __builtin_amdgcn_readfirstlane(lds_addr(la) + w * 64 * TK);
+    const uint32_t b0 = __builtin_amdgcn_readfirstlane(lds_addr(lb) + w * 64 * TK);
+    const uint8_t* ab = uniform_ptr(abase);
+    const uint8_t* bb = uniform_ptr(bbase);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dma16(ab, aoffs[j], a0 + j * 8 * TK);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dma16(bb, boffs[j], b0 + j * 8 * TK);
+}
+
+// One 64-wide K step: fragments of 4 A and 4 B blocks from LDS (two 16-byte
+// granules each: K offsets c0 and c1 of the step), then 16 scaled MFMAs with
+// scale byte OPSEL of each lane's scale dword.
+template <int OPSEL>
+__device__ __forceinline__ void compute_step(const uint8_t* la, const uint8_t* lb, const int (&aoff)[4],
+                                             const int (&boff)[4], int c0, int c1, const uint32_t (&sa)[4],
+                                             const uint32_t (&sb)[4], f32x16 (&acc)[4][4]) {
+    i32x8 af[4], bf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(la + aoff[i] + c0);
+        const uint4 hi = *reinterpret_cast<const uint4*>(la + aoff[i] + c1);
+        af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(lb + boff[j] + c0);
+        const uint4 hi = *reinterpret_cast<const uint4*>(lb + boff[j] + c1);
+        bf[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, OPSEL,
+                                                                       (int)sa[i], OPSEL, (int)sb[j]);
+}
+
+// One 128-wide K stage = two steps, op_sel OPSEL0 and OPSEL0 + 1.
+template <int OPSEL0>
+__device__ __forceinline__ void compute_stage(const uint8_t* la, const uint8_t* lb, const int (&aoff)[4],
+                                              const int (&boff)[4], int x00, int x01, int x10, int x11,
+                                              const uint32_t (&sa)[4], const uint32_t (&sb)[4],
+                                              f32x16 (&acc)[4][4]) {
+    compute_step<OPSEL0>(la, lb, aoff, boff, x00, x01, sa, sb, acc);
+    compute_step<OPSEL0 + 1>(la, lb, aoff, boff, x10, x11, sa, sb, acc);
+}
+
+__device__ __forceinline__ void run_tile_impl(const Tile& T, uint8_t* __restrict__ la0, uint8_t* __restrict__ la1,
+                                              uint8_t* __restrict__ lb0, uint8_t* __restrict__ lb1) {
+    const int t = threadIdx.x;
+    const int w = t >> 6;
+    const int l = t & 63;
+    const int wm = w >> 1, wn = w & 1;
+    const int h = l >> 5, r32 = l & 31;
+
+    // Tile bases (uniform) and per-lane 32-bit row offsets.  Rows past the
+    // operand's limit read its last row instead; their results are dropped.
+    const uint8_t* abase = T.A + T.a_row0 * T.lda;
+    const uint8_t* bbase = T.B + T.b_row0 * T.ldb;
+    uint32_t aoffs[8], boffs[8];
+    {
+        const int gran = ((l & 7) ^ (l >> 3)) * 16;  // logical granule stored at physical l%8
+        const int64_t alast = T.a_lim - 1 - T.a_row0, blast = T.b_lim - 1 - T.b_row0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t rr = w * 64 + j * 8 + (l >> 3);
+            aoffs[j] = (uint32_t)((rr < alast ? rr : alast) * T.lda + gran);
+            boffs[j] = (uint32_t)((rr < blast ? rr : blast) * T.ldb + gran);
+        }
+    }
+    // fragment offsets in LDS and granule offsets of the two 64-wide steps
+    int aoff[4], boff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        aoff[i] = (wm * 128 + i * 32 + r32) * TK;
+        boff[i] = (wn * 128 + i * 32 + r32) * TK;
+    }
+    const int sw = r32 & 7;
+    const int x00 = ((0 + h) ^ sw) * 16, x01 = ((2 + h) ^ sw) * 16;
+    const int x10 = ((4 + h) ^ sw) * 16, x11 = ((6 + h) ^ sw) * 16;
+    // scale dword offsets (chunk 0) from the packed arrays' bases
+    uint32_t saoff[4], sboff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t ra = clamp64(T.a_row0 + wm * 128 + i * 32 + r32, 0, T.a_lim - 1);
+        const int64_t rb = clamp64(T.b_row0 + wn * 128 + i * 32 + r32, 0, T.b_lim - 1);
+        saoff[i] = (uint32_t)((ra >> 5) * T.a_unit + 4 * (32 * h + (ra & 31)));
+        sboff[i] = (uint32_t)((rb >> 5) * T.b_unit + 4 * (32 * h + (rb & 31)));
+    }
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    const int64_t nchunk = (T.k1 - T.k0) / 256;
+    if (nchunk > 0) {
+        uint32_t sa[4], sb[4], na[4], nb[4];
+        const uint8_t* As = T.As + (T.k0 / 256) * 256;
+        const uint8_t* Bs = T.Bs + (T.k0 / 256) * 256;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            na[i] = *reinterpret_cast<const uint32_t*>(As + saoff[i]);
+            nb[i] = *reinterpret_cast<const uint32_t*>(Bs + sboff[i]);
+        }
+        issue_stage(abase + T.k0, bbase + T.k0, aoffs, boffs, la0, lb0, w);
+        for (int64_t c = 0; c < nchunk; ++c) {
+            const int64_t kc = T.k0 + c * 256;
+            // first half of the chunk: buffer 0, op_sel 0/1
+            wait_vmem_all();
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sa[i] = na[i];
+                sb[i] = nb[i];
+            }
+            issue_stage(abase + kc + TK, bbase + kc + TK, aoffs, boffs, la1, lb1, w);
+            if (c + 1 < nchunk) {
+                As += 256;
+                Bs += 256;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    na[i] = *reinterpret_cast<const uint32_t*>(As + saoff[i]);
+                    nb[i] = *reinterpret_cast<const uint32_t*>(Bs + sboff[i]);
+                }
+            }
+            compute_stage<0>(la0, lb0, aoff, boff, x00, x01, x10, x11, sa, sb, acc);
+            pin_acc(acc);
+            // second half: buffer 1, op_sel 2/3
+            wait_vmem_all();
+            __syncthreads();
+            if (c + 1 < nchunk) issue_stage(abase + kc + 256, bbase + kc + 256, aoffs, boffs, la0, lb0, w);
+            compute_stage<2>(la1, lb1, aoff, boff, x00, x01, x10, x11, sa, sb, acc);
+            pin_acc(acc);
+        }
+    }
+    // epilogue: lane holds column r32 of each 32 x 32 block, rows
+    // 8*(e/4) + 4*h + e%4.  The lane bases are made opaque here so that the
+    // compiler does not hoist all 256 row/address values out of the
+    // persistent tile loop (which would not fit in registers).
+    int rb = wm * 128 + 4 * h;
+    int cb = wn * 128 + r32;
+    uint32_t ldo = (uint32_t)T.ldo;
+    asm volatile("" : "+v"(rb), "+v"(cb), "+s"(ldo));
+    uint16_t* const o = T.out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int col = cb + j * 32;
+        if (col >= T.cols) continue;
+        uint16_t* const oc = o + col;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = rb + i * 32 + 8 * (e >> 2) + (e & 3);
+                if (row < T.rows) {
+                    const __bf16 v = (__bf16)acc[i][j][e];
+                    oc[(uint32_t)row * ldo] = __builtin_bit_cast(uint16_t, v);
+                }
+            }
+    }
+    // the next tile reuses the LDS buffers
+    __syncthreads();
+}
+
+__device__ __forceinline__ void run_tile(const Tile& T) { run_tile_impl(T, lds_a0, lds_a1, lds_b0, lds_b1); }
+
+__device__ __forceinline__ int64_t group_lo(const int32_t* off, int g, int64_t M) {
+    return clamp64(off[g], 0, M);
+}
+
+__global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs a) {
+    const int t = threadIdx.x;
+    const int nwg = gridDim.x;
+    const int bid = blockIdx.x;
+    // workgroup -> slot so that each XCD (bid % 8) owns a contiguous slot range
+    const int slot = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
+
+    if (a.mode != 1) {
+        const int64_t nN = (a.N + TN - 1) / TN;
+        // per-group tile counts and their inclusive prefix (16 per thread)
+        const int G = a.G;
+        int32_t loc[16];
+        int32_t sum = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int g = t * 16 + j;
+            int32_t cnt = 0;
+            if (g < G) {
+                const int64_t lo = group_lo(a.offsets, g, a.M), hi = group_lo(a.offsets, g + 1, a.M);
+                const int64_t mg = hi > lo ? hi - lo : 0;
+                cnt = (int32_t)(((mg + TM - 1) / TM) * nN);
+            }
+            sum += cnt;
+            loc[j] = sum;
+        }
+        __shared__ int32_t part[256];
+        part[t] = sum;
+        __syncthreads();
+        for (int d = 1; d < 256; d <<= 1) {
+            const int32_t v = t >= d ? part[t - d] : 0;
+            __syncthreads();
+            part[t] += v;
+            __syncthreads();
+        }
+        const int32_t base = part[t] - sum;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (t * 16 + j < G) tile_end[t * 16 + j] = base + loc[j];
+        __syncthreads();
+        const int32_t total = G > 0 ? tile_end[G - 1] : 0;
+
+        for (int64_t tile = slot; tile < total; tile += nwg) {
+            // group: first g with tile_end[g] > tile
+            int lo = 0, hi = G - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (tile_end[mid] > tile) hi = mid;
+                else lo = mid + 1;
+            }
+            const int g = lo;
+            const int64_t first = g > 0 ? tile_end[g - 1] : 0;
+            const int64_t local = tile - first;
+            const int64_t o0 = group_lo(a.offsets, g, a.M);
+            const int64_t o1 = group_lo(a.offsets, g + 1, a.M);
+            const int64_t mg = o1 - o0;
+            const int64_t nM = (mg + TM - 1) / TM;
+            const int64_t band = local / (kBand * nN);
+            const int64_t gm = (nM - band * kBand) < kBand ? (nM - band * kBand) : kBand;
+            const int64_t r = local - band * kBand * nN;
+            const int64_t mt = band * kBand + r % gm;
+            const int64_t nt = r / gm;
+
+            Tile T;
+            T.A = a.A;
+            T.As = a.As;
+            T.lda = a.K;
+            T.a_unit = 32 * (a.K / 32);
+            T.a_row0 = o0 + mt * TM;
+            T.a_lim = o1;
+            if (a.mode == 0) {
+                // expert g's weights: rows [g N, g N + N) of the [G N][K] matrix
+                T.B = a.B;
+                T.Bs = a.Bs;
+                T.ldb = a.K;
+                T.b_unit = 32 * (a.K / 32);
+                T.b_row0 = (int64_t)g * a.N + nt * TN;
+                T.b_lim = (int64_t)g * a.N + a.N;
+            } else {
+                // transposed weights [N][ldb]: expert g is the column slice
+                // [g K, g K + K), i.e. its contraction starts g K bytes (g K / 256
+                // scale chunks) into every row
+                T.B = a.B + (int64_t)g * a.K;
+                T.Bs = a.Bs + ((int64_t)g * a.K / 256) * 256;
+                T.ldb = a.ldb;
+                T.b_unit = 32 * (a.ldb / 32);
+                T.b_row0 = nt * TN;
+                T.b_lim = a.N;
+            }
+            T.k0 = 0;
+            T.k1 = a.K;
+            T.out = a.out + (o0 + mt * TM) * a.N + nt * TN;
+            T.ldo = a.N;
+            T.rows = (int32_t)((mg - mt * TM) < TM ? (mg - mt * TM) : TM);
+            T.cols = (int32_t)((a.N - nt * TN) < TN ? (a.N - nt * TN) : TN);
+            run_tile(T);
+        }
+    } else {
+        // wgrad: every group has the same tile grid over [N] x [K]
+        const int64_t nMt = (a.N + TM - 1) / TM;
+        const int64_t nNt = (a.K + TN - 1) / TN;
+        const int64_t per = nMt * nNt;
+        const int64_t total = per * a.G;
+        for (int64_t tile = slot; tile < total; tile += nwg) {
+            const int64_t g = tile / per;
+            const int64_t local = tile - g * per;
+            const int64_t band = local / (kBand * nNt);
+            const int64_t gm = (nMt - band * kBand) < kBand ? (nMt - band * kBand) : kBand;
+            const int64_t r = local - band * kBand * nNt;
+            const int64_t mt = band * kBand + r % gm;
+            const int64_t nt = r / gm;
+            int64_t p0 = clamp64(a.offsets[g], 0, a.Mcap) & ~(int64_t)255;
+            int64_t p1 = clamp64(a.offsets[g + 1], 0, a.Mcap) & ~(int64_t)255;
+            if (p1 < p0) p1 = p0;
+
+            Tile T;
+            T.A = a.A;
+            T.As = a.As;
+            T.lda = a.Mcap;
+            T.a_unit = 32 * (a.Mcap / 32);
+            T.a_row0 = mt * TM;
+            T.a_lim = a.N;
+            T.B = a.B;
+            T.Bs = a.Bs;
+            T.ldb = a.Mcap;
+            T.b_unit = 32 * (a.Mcap / 32);
+            T.b_row0 = nt * TN;
+            T.b_lim = a.K;
+            T.k0 = p0;
+            T.k1 = p1;
+            T.out = a.out + g * a.N * a.K + mt * TM * a.K + nt * TN;
+            T.ldo = a.K;
+            T.rows = (int32_t)((a.N - mt * TM) < TM ? (a.N - mt * TM) : TM);
+            T.cols = (int32_t)((a.K - nt * TN) < TN ? (a.K - nt * TN) : TN);
+            run_tile(T);
+        }
+    }
+}
+
+int num_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+}  // namespace
+
+hipError_t launch_grouped_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq,
+                               const uint8_t* Ws, const int32_t* group_offsets, int32_t G, int64_t M,
+                               int64_t N, int64_t K, uint16_t* out, hipStream_t stream) {
+    if (M == 0 || N == 0) return hipSuccess;
+    GemmArgs a;
+    a.A = Xq;
+    a.As = Xs;
+    a.B = Wq;
+    a.Bs = Ws;
+    a.offsets = group_offsets;
+    a.out = out;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.Mcap = 0;
+    a.G = G;
+    a.mode = 0;
+    a.ldb = 0;
+    const int64_t ub = ((M + TM - 1) / TM + G) * ((N + TN - 1) / TN);
+    int64_t nwg = num_cus();
+    if (ub < nwg) nwg = ub;
+    hipLaunchKernelGGL(grouped_gemm_kernel, dim3((unsigned)nwg), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm_dgrad(const uint8_t* dYq, const uint8_t* dYs, const uint8_t* WTq,
+                                     const uint8_t* WTs, const int32_t* group_offsets, int32_t G, int64_t M,
+                                     int64_t N, int64_t K, int64_t Wcap, uint16_t* dX, hipStream_t stream) {
+    if (M == 0 || N == 0) return hipSuccess;
+    GemmArgs a;
+    a.A = dYq;
+    a.As = dYs;
+    a.B = WTq;
+    a.Bs = WTs;
+    a.offsets = group_offsets;
+    a.out = dX;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.Mcap = 0;
+    a.G = G;
+    a.mode = 2;
+    a.ldb = Wcap;
+    const int64_t ub = ((M + TM - 1) / TM + G) * ((N + TN - 1) / TN);
+    int64_t nwg = num_cus();
+    if (ub < nwg) nwg = ub;
+    hipLaunchKernelGGL(grouped_gemm_kernel, dim3((unsigned)nwg), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm_wgrad(const uint8_t* A, const uint8_t* As, const uint8_t* B,
+                                     const uint8_t* Bs, const int32_t* padded_offsets, int32_t G,
+                                     int64_t N, int64_t K, int64_t Mcap, uint16_t* dW,
+                                     hipStream_t stream) {
+    if (N == 0 || K == 0 || G == 0) return hipSuccess;
+    GemmArgs a;
+    a.A = A;
+    a.As = As;
+    a.B = B;
+    a.Bs = Bs;
+    a.offsets = padded_offsets;
+    a.out = dW;
+    a.M = 0;
+    a.N = N;
+    a.K = K;
+    a.Mcap = Mcap;
+    a.G = G;
+    a.mode = 1;
+    a.ldb = 0;
+    const int64_t total = ((N + TM - 1) / TM) * ((K + TN - 1) / TN) * G;
+    int64_t nwg = num_cus();
+    if (total < nwg) nwg = total;
+    hipLaunchKernelGGL(grouped_gemm_kernel, dim3((unsigned)nwg), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace mx

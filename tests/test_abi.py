@@ -1,0 +1,105 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects invalid arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp8_block_scaled_04_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libmxmoe.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mx_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_header_symbol():
+    lib = mx.load()
+    names = header_functions()
+    assert names, "no declarations parsed"
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(mx.SYMBOLS) == names
+
+
+def test_host_helpers():
+    assert mx.mx_scale_bytes(40, 512) == 1024
+    assert mx.mx_scale_bytes(131072, 7168) == 131072 * 224
+    assert mx.mx_scale_bytes(1, 32) == 32 * 8
+    assert mx.mx_cols_capacity(300, 3) == 256 * (2 + 2)
+    assert mx.mx_cols_capacity(32768, 16) == 256 * (128 + 15)
+    assert mx.mx_cols_capacity(0, 1) == 0
+    assert mx.load().mx_cols_capacity(5, 0) == -1
+    assert mx.status_str(0) == "MX_OK" and mx.status_str(6) == "MX_ERR_HIP"
+
+
+P = ctypes.c_void_p
+FAKE = P(0x100000)  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize(
+    "args,want",
+    [
+        ((FAKE, 4, 33, 40, FAKE, FAKE, None), 2),   # K % 32 != 0
+        ((FAKE, -1, 32, 32, FAKE, FAKE, None), 2),  # negative M
+        ((FAKE, 4, 64, 32, FAKE, FAKE, None), 2),   # ldx < K
+        ((None, 4, 32, 32, FAKE, FAKE, None), 1),   # NULL x
+        ((FAKE, 4, 32, 32, None, FAKE, None), 1),   # NULL q
+        ((P(0x100004), 4, 32, 32, FAKE, FAKE, None), 3),  # misaligned x
+        ((FAKE, 4, 32, 36, FAKE, FAKE, None), 3),   # ldx not a multiple of 8
+        ((None, 0, 32, 32, None, None, None), 0),   # M == 0: no work, OK
+    ],
+)
+def test_quantize_rows_validation(args, want):
+    assert mx.load().mx_quantize_rows(*args) == want
+
+
+def test_quantize_cols_validation():
+    f = mx.load().mx_quantize_cols
+    cap = mx.mx_cols_capacity(300, 3)
+    assert f(FAKE, 300, 64, 64, FAKE, 3, FAKE, FAKE, cap - 256, FAKE, None) == 4  # capacity too small
+    assert f(FAKE, 300, 64, 64, FAKE, 3, FAKE, FAKE, cap + 8, FAKE, None) == 4    # not multiple of 256
+    assert f(FAKE, 300, 60, 64, FAKE, 3, FAKE, FAKE, cap, FAKE, None) == 5        # N % 8 != 0
+    assert f(FAKE, 300, 64, 64, FAKE, 0, FAKE, FAKE, cap, FAKE, None) == 2        # G < 1
+    assert f(FAKE, 300, 64, 64, FAKE, 5000, FAKE, FAKE, 256 * 6000, FAKE, None) == 2  # G too large
+    assert f(FAKE, 300, 64, 64, FAKE, 3, FAKE, FAKE, cap, None, None) == 1        # padded offsets required
+    assert f(FAKE, 300, 64, 32, FAKE, 3, FAKE, FAKE, cap, FAKE, None) == 2        # ldx < N
+
+
+def test_grouped_gemm_validation():
+    f = mx.load().mx_grouped_gemm
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 128, 288, FAKE, None) == 5  # K % 256 != 0
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 128, 250, FAKE, None) == 2  # K % 32 != 0
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 512, 128, 256, FAKE, None) == 2  # G < 1
+    assert f(FAKE, FAKE, None, FAKE, FAKE, 4, 512, 128, 256, FAKE, None) == 1  # NULL W
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 4, 512, 128, 256, FAKE, None) == 1  # NULL offsets
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 128, 256, P(0x100002), None) == 3  # misaligned out
+    assert f(None, None, None, None, None, 4, 0, 128, 256, None, None) == 0    # M == 0: no work
+
+
+def test_dgrad_validation():
+    f = mx.load().mx_grouped_gemm_dgrad
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 64, 512, 1024, FAKE, None) == 4   # Wcap < G*K
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 64, 288, 2048, FAKE, None) == 5   # K % 256
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 4, 512, 64, 512, 2048, FAKE, None) == 1   # NULL offsets
+    assert f(None, None, None, None, None, 4, 0, 64, 512, 2048, None, None) == 0     # M == 0
+
+
+def test_wgrad_validation():
+    f = mx.load().mx_grouped_gemm_wgrad
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 64, 300, FAKE, None) == 4   # Mcap % 256
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 4, 64, 64, 512, FAKE, None) == 1  # NULL offsets
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 64, 512, FAKE, None) == 2  # G < 1
+    assert f(None, None, None, None, None, 4, 0, 64, 512, None, None) == 0   # N == 0: no work
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(mx, "_lib", None)
+    monkeypatch.setattr(mx, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError):
+        mx.load()

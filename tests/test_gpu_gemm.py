@@ -1,0 +1,232 @@
+"""GPU parity of the grouped GEMM kernels against the fp64 oracle:
+|gpu - ref| <= 8e-3 |ref| + 1e-3 rms(ref) for every checked element (the
+bf16 output rounding alone contributes up to 2^-9 |ref|), and bit-exact
+results where the exact product is representable in bf16 (one-hot weights).
+Operands are quantized by the GPU kernels, whose bytes are first checked
+against the oracle's."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_block_scaled_04_amd as mx
+import oracle
+from mxfp8_block_scaled_04_amd import workloads as W
+from tests.mxtest import bits, bf16_to_f64, canonical_scales, gemm_tolerance_ok, sample_points, u8
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+NAN_BF16 = 0x7FC0
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    mx.load()
+
+
+def quantize_pair(x, w):
+    """Quantize X [M, K] and W [G, N, K] on the GPU; check the bytes of a few
+    rows against the oracle; return device tensors + canonical host copies."""
+    G, N, K = w.shape
+    Xq, Xs = mx.mx_quantize_rows(x)
+    Wq, Ws = mx.mx_quantize_rows(w.reshape(G * N, K))
+    torch.cuda.synchronize()
+    return Xq, Xs, Wq.reshape(G, N, K), Ws
+
+
+def host_operands(Xq, Xs, Wq, Ws):
+    M, K = Xq.shape
+    G, N, _ = Wq.shape
+    return (u8(Xq), canonical_scales(Xs, M, K), u8(Wq), canonical_scales(Ws, G * N, K).reshape(G, N, K // 32))
+
+
+def nan_filled(shape):
+    return torch.full(shape, NAN_BF16, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+
+
+def test_gemm_tiny_moe_full():
+    d = W.tiny_moe(seed=0, device=DEV)
+    Xq, Xs, Wq, Ws = quantize_pair(d["x"], d["w"])
+    off = torch.from_numpy(d["offsets"]).to(DEV)
+    out = mx.mx_grouped_gemm(Xq, Xs, Wq, Ws, off, out=nan_filled((d["M"], d["N"])))
+    torch.cuda.synchronize()
+    hx, hxs, hw, hws = host_operands(Xq, Xs, Wq, Ws)
+    # the GPU-quantized operands are the oracle's own
+    q_ref, s_ref = oracle.quantize_rows(bits(d["x"]))
+    assert np.array_equal(hx, q_ref) and np.array_equal(hxs, s_ref)
+    ref = oracle.grouped_gemm(hx, hxs, hw, hws, d["offsets"])
+    got = bf16_to_f64(out)
+    ok, ratio = gemm_tolerance_ok(got, ref)
+    assert ok, ratio
+
+
+def test_gemm_one_hot_bit_exact():
+    """One nonzero weight per output column: each output is a single product
+    of two E4M3 values times two powers of two, exact in bf16."""
+    rng = np.random.default_rng(3)
+    M, N, K, G = 300, 200, 512, 3
+    sizes = [120, 0, 180]
+    off = W.offsets_from_sizes(sizes)
+    x = torch.from_numpy((rng.standard_normal((M, K)) * 4).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    w = np.zeros((G, N, K), np.float32)
+    k0 = rng.integers(0, K, (G, N))
+    vals = rng.choice([1.0, -2.0, 0.5, 1.5, -3.0, 0.25], (G, N))
+    for g in range(G):
+        for n in range(N):
+            w[g, n, k0[g, n]] = vals[g, n]
+    wt = torch.from_numpy(w).to(torch.bfloat16).to(DEV)
+    Xq, Xs, Wq, Ws = quantize_pair(x, wt)
+    out = mx.mx_grouped_gemm(Xq, Xs, Wq, Ws, torch.from_numpy(off).to(DEV), out=nan_filled((M, N)))
+    torch.cuda.synchronize()
+    hx, hxs, hw, hws = host_operands(Xq, Xs, Wq, Ws)
+    ref = oracle.grouped_gemm(hx, hxs, hw, hws, off)
+    ref_bf16 = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16)
+    assert torch.equal(ref_bf16.float(), torch.from_numpy(ref.astype(np.float32)))  # exact in bf16
+    assert np.array_equal(bits(out), bits(ref_bf16))
+
+
+@pytest.mark.parametrize("sizes,N,K", [([1, 31, 33, 0, 257, 5], 72, 512), ([0, 0, 700], 300, 256), ([513], 256, 768), ([40] * 10, 40, 256)])
+def test_gemm_ragged_full(sizes, N, K):
+    M, G = sum(sizes), len(sizes)
+    off = W.offsets_from_sizes(sizes)
+    x = W.normal_bf16((M, K), 1.0, M + N, DEV)
+    w = W.normal_bf16((G, N, K), 0.02, M + K, DEV)
+    Xq, Xs, Wq, Ws = quantize_pair(x, w)
+    out = mx.mx_grouped_gemm(Xq, Xs, Wq, Ws, torch.from_numpy(off).to(DEV), out=nan_filled((M, N)))
+    torch.cuda.synchronize()
+    ref = oracle.grouped_gemm(*host_operands(Xq, Xs, Wq, Ws), off)
+    ok, ratio = gemm_tolerance_ok(bf16_to_f64(out), ref)
+    assert ok, ratio
+
+
+def test_gemm_zero_rows_is_noop():
+    Xq = torch.empty((0, 256), dtype=torch.uint8, device=DEV)
+    Xs = torch.empty(0, dtype=torch.uint8, device=DEV)
+    Wq = torch.zeros((2, 64, 256), dtype=torch.uint8, device=DEV)
+    Ws = torch.zeros(mx.mx_scale_bytes(128, 256), dtype=torch.uint8, device=DEV)
+    off = torch.zeros(3, dtype=torch.int32, device=DEV)
+    out = mx.mx_grouped_gemm(Xq, Xs, Wq, Ws, off)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64)
+
+
+def sampled_check(x, w, sizes, seed):
+    M, K = x.shape
+    G, N, _ = w.shape
+    off = W.offsets_from_sizes(sizes)
+    Xq, Xs, Wq, Ws = quantize_pair(x, w)
+    out = mx.mx_grouped_gemm(Xq, Xs, Wq, Ws, torch.from_numpy(off).to(DEV), out=nan_filled((M, N)))
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any().item(), "an output row was not written"
+    rows, cols = sample_points(np.random.default_rng(seed), M, N, off)
+    ref = oracle.grouped_gemm_points(*host_operands(Xq, Xs, Wq, Ws), off, rows, cols)
+    got = bf16_to_f64(out[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)])
+    ok, ratio = gemm_tolerance_ok(got, ref)
+    assert ok, ratio
+    return out
+
+
+def test_gemm_gate_up_sampled():
+    d = W.moe_gate_up(seed=0, device=DEV)
+    sampled_check(d["x"], d["w"], d["sizes"], 0)
+
+
+def test_gemm_ragged_and_dense_sampled():
+    d = W.moe_ragged(seed=0, device=DEV)
+    sampled_check(d["x"], d["w"], d["sizes"], 1)
+    sampled_check(d["x"], d["w_dense"], [d["M"]], 2)
+
+
+def test_gemm_down_forward_sampled():
+    d = W.moe_down_backward(seed=0, device=DEV)
+    sampled_check(d["x"], d["w"], d["sizes"], 3)
+
+
+def dgrad_check(dy, w, sizes, seed, sample=True):
+    """dX = dY W per expert: dY row-quantized along N_out; W^T from the
+    column-wise quantization of W viewed as [G*N_out, K_in] with one group per
+    expert, consumed in place by mx_grouped_gemm_dgrad."""
+    G, Nout, Kin = w.shape
+    M = dy.shape[0]
+    dyq, dys = mx.mx_quantize_rows(dy)
+    woff_h = (np.arange(G + 1) * Nout).astype(np.int32)
+    wT, wTs, P = mx.mx_quantize_cols(w.reshape(G * Nout, Kin), torch.from_numpy(woff_h).to(DEV))
+    off = W.offsets_from_sizes(sizes)
+    out = mx.mx_grouped_gemm_dgrad(dyq, dys, wT, wTs, torch.from_numpy(off).to(DEV), G, out=nan_filled((M, Kin)))
+    torch.cuda.synchronize()
+    assert np.array_equal(P.cpu().numpy(), woff_h)
+    assert not torch.isnan(out).any().item()
+    Wcap = wT.shape[1]
+    # oracle operands: W^T of expert g = columns [g Nout, (g+1) Nout) of the
+    # column-quantized weights, as a [G, Kin, Nout] stack
+    wT_h = u8(wT)
+    wTs_h = canonical_scales(wTs, Kin, Wcap)
+    Bq = np.stack([wT_h[:, g * Nout:(g + 1) * Nout] for g in range(G)])
+    Bs = np.stack([wTs_h[:, g * Nout // 32:(g + 1) * Nout // 32] for g in range(G)])
+    if sample:
+        rows, cols = sample_points(np.random.default_rng(seed), M, Kin, off)
+    else:
+        rows, cols = [a.ravel() for a in np.meshgrid(np.arange(M), np.arange(Kin), indexing="ij")]
+    ref = oracle.grouped_gemm_points(u8(dyq), canonical_scales(dys, M, Nout), Bq, Bs, off, rows, cols)
+    got = bf16_to_f64(out[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)])
+    ok, ratio = gemm_tolerance_ok(got, ref)
+    assert ok, ratio
+
+
+def test_gemm_dgrad_small_full():
+    sizes = [5, 0, 300, 40]
+    G, Nout, Kin = 4, 512, 72
+    dy = W.normal_bf16((sum(sizes), Nout), 1.0, 21, DEV)
+    w = W.normal_bf16((G, Nout, Kin), 0.02, 22, DEV)
+    dgrad_check(dy, w, sizes, 0, sample=False)
+
+
+def test_gemm_dgrad_sampled():
+    d = W.moe_down_backward(seed=0, device=DEV)
+    dgrad_check(d["dy"], d["w"], d["sizes"], 4)
+
+
+@pytest.mark.parametrize("sizes,N,K", [([5, 0, 300, 40], 64, 48), ([256], 296, 264), ([0, 0], 32, 32), ([700, 1], 256, 256)])
+def test_wgrad_full(sizes, N, K):
+    M = sum(sizes)
+    off = W.offsets_from_sizes(sizes)
+    dy = W.normal_bf16((M, N), 1.0, 11 + M, DEV)
+    x = W.normal_bf16((M, K), 1.0, 12 + M, DEV)
+    off_dev = torch.from_numpy(off).to(DEV)
+    A, As, P = mx.mx_quantize_cols(dy, off_dev)
+    B, Bs, P2 = mx.mx_quantize_cols(x, off_dev)
+    G = len(sizes)
+    dW = mx.mx_grouped_gemm_wgrad(A, As, B, Bs, P, dW=nan_filled((G, N, K)))
+    torch.cuda.synchronize()
+    Mcap = A.shape[1]
+    Aq, Asc, Pr = oracle.quantize_cols(bits(dy), off, Mcap)
+    Bq, Bsc, _ = oracle.quantize_cols(bits(x), off, Mcap)
+    assert np.array_equal(u8(A), Aq) and np.array_equal(u8(B), Bq)
+    ref = oracle.wgrad(Aq, Asc, Bq, Bsc, Pr)
+    ok, ratio = gemm_tolerance_ok(bf16_to_f64(dW), ref)
+    assert ok, ratio
+    for g in range(G):
+        if sizes[g] == 0:
+            assert torch.count_nonzero(dW[g].float()).item() == 0
+
+
+def test_wgrad_down_backward_sampled():
+    d = W.moe_down_backward(seed=0, device=DEV)
+    off = d["offsets"]
+    off_dev = torch.from_numpy(off).to(DEV)
+    A, As, P = mx.mx_quantize_cols(d["dy"], off_dev)
+    B, Bs, _ = mx.mx_quantize_cols(d["x"], off_dev)
+    G, N, K = d["G"], d["N"], d["K"]
+    dW = mx.mx_grouped_gemm_wgrad(A, As, B, Bs, P, dW=nan_filled((G, N, K)))
+    torch.cuda.synchronize()
+    assert not torch.isnan(dW).any().item()
+    Mcap = A.shape[1]
+    rng = np.random.default_rng(5)
+    gs = np.concatenate([rng.integers(0, G, 2048), np.arange(G)])
+    ns = np.concatenate([rng.integers(0, N, 2048), np.full(G, N - 1)])
+    ks = np.concatenate([rng.integers(0, K, 2048), np.full(G, K - 1)])
+    ref = oracle.wgrad_points(u8(A), canonical_scales(As, N, Mcap), u8(B), canonical_scales(Bs, K, Mcap),
+                              P.cpu().numpy(), gs, ns, ks)
+    got = bf16_to_f64(dW[torch.from_numpy(gs).to(DEV), torch.from_numpy(ns).to(DEV), torch.from_numpy(ks).to(DEV)])
+    ok, ratio = gemm_tolerance_ok(got, ref)
+    assert ok, ratio

@@ -1,0 +1,155 @@
+"""GPU parity of the quantize kernels against the CPU oracle: fp8 codes and
+E8M0 scales must match bit for bit (lpnh.cn 2479732 section 1: one scale per
+32-element block, divide, cast to E4M3; scale rule floor(log2 amax) - 8,
+saturation to +/-448, round to nearest even)."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_block_scaled_04_amd as mx
+import oracle
+from mxfp8_block_scaled_04_amd import workloads as W
+from tests.mxtest import bits, canonical_scales, u8
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    mx.load()
+
+
+def check_rows(x_dev, ldx_cols=None):
+    """Quantize x_dev [M, K] row-wise on the GPU and compare with the oracle."""
+    M, K = x_dev.shape
+    q, s = mx.mx_quantize_rows(x_dev)
+    torch.cuda.synchronize()
+    xb = bits(x_dev)
+    q_ref, s_ref = oracle.quantize_rows(xb)
+    q_gpu = u8(q)
+    assert np.array_equal(q_gpu, q_ref), np.argwhere(q_gpu != q_ref)[:5]
+    s_gpu = u8(s)
+    assert s_gpu.size == oracle.packed_scale_bytes(M, K)
+    assert np.array_equal(s_gpu, oracle.pack_scales(s_ref, K))  # pads included
+
+
+def test_rows_tiny_moe():
+    d = W.tiny_moe(seed=0, device=DEV)
+    check_rows(d["x"])
+    check_rows(d["w"].reshape(-1, d["K"]))
+
+
+@pytest.mark.parametrize("M,K,ldx", [(1, 32, 32), (45, 288, 296), (33, 7168, 7168), (100, 2080, 2096), (64, 256, 256)])
+def test_rows_ragged_shapes(M, K, ldx):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(M * 1000 + K)
+    base = torch.randn((M, ldx), generator=g, device=DEV) * torch.exp2(torch.randint(-20, 20, (M, 1), generator=g, device=DEV).float())
+    x = base.to(torch.bfloat16)[:, :K]
+    check_rows(x)
+
+
+def _exhaustive_blocks():
+    """Every (bf16 pattern, S) pair the quantizer can see: for each S, an
+    anchor of exponent field S + 8 in slot 0 fixes the block scale, and the
+    other 31 slots run through every pattern (both signs) of exponent field
+    <= S + 8.  S = 0 blocks have no anchor (their max field is <= 8)."""
+    blocks = []
+    for S in range(0, 247):
+        emax = S + 8
+        pats = np.arange(0, (emax + 1) << 7, dtype=np.uint32)
+        pats = np.concatenate([pats, pats | 0x8000]).astype(np.uint16)
+        per = 31 if S > 0 else 32
+        n = (pats.size + per - 1) // per
+        padded = np.zeros(n * per, np.uint16)
+        padded[: pats.size] = pats
+        body = padded.reshape(n, per)
+        if S > 0:
+            anchor = np.full((n, 1), emax << 7, np.uint16)
+            body = np.concatenate([anchor, body], axis=1)
+        blocks.append(body)
+    allb = np.concatenate(blocks, axis=0)
+    rows = (allb.shape[0] + 31) // 32
+    pad = np.zeros((rows * 32 - allb.shape[0], 32), np.uint16)
+    return np.concatenate([allb, pad]).reshape(rows, 32 * 32)
+
+
+def test_rows_element_map_exhaustive():
+    xb = _exhaustive_blocks()
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(DEV)
+    q, s = mx.mx_quantize_rows(x)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_rows(xb)
+    assert np.array_equal(u8(q), q_ref), np.argwhere(u8(q) != q_ref)[:5]
+    assert np.array_equal(canonical_scales(s, *xb.shape), s_ref)
+    assert set(np.unique(s_ref).tolist()) == set(range(0, 247))
+
+
+def test_rows_quant_bandwidth_sampled():
+    x = W.quant_bandwidth(seed=0, device=DEV)
+    M, K = x.shape
+    q, s = mx.mx_quantize_rows(x)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 1, M - 1], rng.integers(0, M, 200)]))
+    xb = bits(x[torch.from_numpy(rows).to(DEV)])
+    q_ref, s_ref = oracle.quantize_rows(xb)
+    assert np.array_equal(u8(q[torch.from_numpy(rows).to(DEV)]), q_ref)
+    s_all = canonical_scales(s, M, K)
+    assert np.array_equal(s_all[rows], s_ref)
+
+
+def check_cols(x_dev, sizes):
+    M, N = x_dev.shape
+    off = None if sizes is None else W.offsets_from_sizes(sizes)
+    off_dev = None if off is None else torch.from_numpy(off).to(DEV)
+    qT, sT, P = mx.mx_quantize_cols(x_dev, off_dev)
+    torch.cuda.synchronize()
+    Mcap = qT.shape[1]
+    q_ref, s_ref, P_ref = oracle.quantize_cols(bits(x_dev), off, Mcap)
+    if P is not None:
+        assert np.array_equal(P.cpu().numpy(), P_ref)
+    assert np.array_equal(u8(qT), q_ref), np.argwhere(u8(qT) != q_ref)[:5]
+    assert np.array_equal(canonical_scales(sT, N, Mcap), s_ref)
+    assert np.count_nonzero(u8(sT)) == np.count_nonzero(s_ref)  # pad bytes are zero
+
+
+@pytest.mark.parametrize("sizes", [[160, 0, 96, 256], [1, 31, 33, 0, 257, 5], [300], [0, 0, 64], [512]])
+def test_cols_groups(sizes):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(sum(sizes) + len(sizes))
+    M = sum(sizes)
+    x = (torch.randn((M, 72), generator=g, device=DEV) * 3).to(torch.bfloat16)
+    check_cols(x, sizes)
+
+
+def test_cols_tiny_moe_and_null_offsets():
+    d = W.tiny_moe(seed=0, device=DEV)
+    check_cols(d["x"], d["sizes"])
+    check_cols(d["x"], None)
+    check_cols(d["x"][:300, :200], None)
+
+
+def test_cols_empty_rows():
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    check_cols(x, [0, 0, 0])
+
+
+def test_cols_down_backward_sampled():
+    d = W.moe_down_backward(seed=0, device=DEV)
+    off = d["offsets"]
+    off_dev = torch.from_numpy(off).to(DEV)
+    for name in ("dy", "x"):
+        x = d[name]
+        M, N = x.shape
+        qT, sT, P = mx.mx_quantize_cols(x, off_dev)
+        torch.cuda.synchronize()
+        Mcap = qT.shape[1]
+        cols = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(1).integers(0, N, 24)]))
+        sub = bits(x[:, torch.from_numpy(cols).to(DEV)])
+        q_ref, s_ref, P_ref = oracle.quantize_cols(sub, off, Mcap)
+        assert np.array_equal(P.cpu().numpy(), P_ref)
+        assert np.array_equal(u8(qT[torch.from_numpy(cols).to(DEV)]), q_ref)
+        s_all = canonical_scales(sT, N, Mcap)
+        assert np.array_equal(s_all[cols], s_ref)
