@@ -251,7 +251,10 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-gemm", action="store_true", help="skip the grouped-GEMM section")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=16384, help="rows of the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=32768, help="rows of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) a few times, "
+                         "so that HBM counters can be scaled against a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -264,6 +267,14 @@ def main():
 
     mx.load()
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
     quant, sample = bench_quant(torch, mx, W, args)
     gemm = None if args.no_gemm else bench_gemm(torch, mx, W, args)
     cpu = None if sample is None else cpu_baseline(sample, args.seed)

@@ -70,7 +70,7 @@ mx_status mx_quantize_cols(const uint16_t* x, int64_t M, int64_t N, int64_t ldx,
         if (!qT || !sT) return MX_ERR_NULL;
         if ((x && !aligned16(x)) || !aligned16(qT) || !aligned16(sT) || ldx % 8 != 0) return MX_ERR_ALIGN;
     }
-    if (Mcap / 256 > (int64_t)UINT32_MAX / 256 || (N + 63) / 64 > 65535) return MX_ERR_UNSUPPORTED;  // grid
+    if (Mcap / 256 > (int64_t)UINT32_MAX / 1024 || (N + 63) / 64 > 65535) return MX_ERR_UNSUPPORTED;  // grid
     return from_hip(mx::launch_quantize_cols(x, M, N, ldx, group_offsets, G, qT, sT, Mcap, padded_offsets,
                                              (hipStream_t)stream));
 }

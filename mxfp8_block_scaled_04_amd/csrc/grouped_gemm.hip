@@ -33,11 +33,11 @@ namespace {
 
 constexpr int TM = 256;
 constexpr int TN = 256;
-constexpr int TK = 128;
-constexpr int kBand = 4;  // M-tiles per band of the tile order
+constexpr int TK = 64;     // K bytes per pipeline stage (one MFMA K step)
+constexpr int NBUF = 4;    // LDS stage buffers; three stages in flight
+constexpr int kBand = 4;   // M-tiles per band of the tile order
 
 typedef __attribute__((address_space(3))) void lds_t;
-typedef __attribute__((address_space(1))) void gbl_t;
 
 struct GemmArgs {
     const uint8_t* A;
@@ -68,23 +68,23 @@ struct Tile {
     int32_t rows, cols;  // valid part of the tile
 };
 
-__shared__ __attribute__((aligned(16))) uint8_t lds_a0[TM * TK];
-__shared__ __attribute__((aligned(16))) uint8_t lds_a1[TM * TK];
-__shared__ __attribute__((aligned(16))) uint8_t lds_b0[TN * TK];
-__shared__ __attribute__((aligned(16))) uint8_t lds_b1[TN * TK];
+__shared__ __attribute__((aligned(16))) uint8_t lds_a[NBUF][TM * TK];
+__shared__ __attribute__((aligned(16))) uint8_t lds_b[NBUF][TN * TK];
+__shared__ __attribute__((aligned(16))) uint32_t lds_sa[2][TM / 32][64];  // scale dwords, [chunk parity][32-row unit][lane]
+__shared__ __attribute__((aligned(16))) uint32_t lds_sb[2][TN / 32][64];
 __shared__ int32_t tile_end[kMaxGroups];  // inclusive prefix of tiles per group
-
-__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
     return v < lo ? lo : (v > hi ? hi : v);
 }
 
-// 16-byte direct global->LDS load (global_load_lds_dwordx4): lane i of the
-// wave writes LDS bytes [lds + 16 i, lds + 16 i + 16).  Issued as inline asm
-// so that the compiler's own wait insertion does not stall every later LDS
-// read on it; completion is enforced explicitly (wait_vmem_all + barrier)
-// before the buffer is read.
+// Stage rows are 64 bytes (4 granules of 16 B).  Granule c of tile row r is
+// stored at position c ^ swz(r): for the fragment reads (rows r..r+15 of one
+// 32-row block, same granule) this puts 8 consecutive rows on 8 distinct
+// 16-byte bank groups of a 128-byte bank line and 16 consecutive rows on 16
+// distinct groups of a 256-byte line.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
 // The address base must be wave-uniform (an SGPR pair).
 __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
     const uint64_t v = (uint64_t)(uintptr_t)p;
@@ -93,14 +93,32 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
     return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
-// M0 is only written here; no other code in these kernels reads it.
+// 16-byte direct global->LDS load (global_load_lds_dwordx4): lane i of the
+// wave writes LDS bytes [lds + 16 i, lds + 16 i + 16).  Issued as inline asm
+// so that the compiler's own wait insertion does not stall every later LDS
+// read on it; completion is enforced explicitly (wait_vm<N> + barrier)
+// before a buffer is read.  M0 is only written here; no other code in these
+// kernels reads it.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
                  : "memory", "m0");
 }
+// 4-byte variant (global_load_lds_dword): lane i writes [lds + 4 i, lds + 4 i + 4).
+__device__ __forceinline__ void dma4(const uint8_t* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Pin the accumulators at this point of the program: the matrix ops that
 // produce them cannot be moved past it (in particular not past the next
@@ -114,39 +132,59 @@ __device__ __forceinline__ void pin_acc(f32x16 (&acc)[4][4]) {
 
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) { return (uint32_t)(uintptr_t)(lds_t*)p; }
 
-// Issue the direct-to-LDS loads of one K stage: this wave's 64 rows of A and
-// of B (8 instructions each, 8 rows x 128 bytes per instruction).  abase and
+// Direct-to-LDS loads of one 64-wide K stage: this wave's 64 rows of A and
+// of B, 4 instructions each (16 rows x 64 bytes per instruction).  abase and
 // bbase are the (uniform) addresses of the tile's first rows at column k.
-__device__ __forceinline__ void issue_stage(const uint8_t* abase, const uint8_t* bbase, const uint32_t (&aoffs)[8],
-                                            const uint32_t (&boffs)[8], uint8_t* la, uint8_t* lb, int w) {
-    const uint32_t a0 = __builtin_amdgcn_readfirstlane(lds_addr(la) + w * 64 * TK);
-    const uint32_t b0 = __builtin_amdgcn_readfirstlane(lds_addr(lb) + w * 64 * TK);
+constexpr int kDmaPerStage = 8;  // vector-memory instructions per wave per stage
+__device__ __forceinline__ void issue_stage(const uint8_t* abase, const uint8_t* bbase, const uint32_t (&aoffs)[4],
+                                            const uint32_t (&boffs)[4], int buf, int w) {
+    const uint32_t a0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_a[buf]) + w * 64 * TK);
+    const uint32_t b0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_b[buf]) + w * 64 * TK);
     const uint8_t* ab = uniform_ptr(abase);
     const uint8_t* bb = uniform_ptr(bbase);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dma16(ab, aoffs[j], a0 + j * 8 * TK);
+    for (int j = 0; j < 4; ++j) dma16(ab, aoffs[j], a0 + j * 16 * TK);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dma16(bb, boffs[j], b0 + j * 8 * TK);
+    for (int j = 0; j < 4; ++j) dma16(bb, boffs[j], b0 + j * 16 * TK);
 }
 
-// One 64-wide K step: fragments of 4 A and 4 B blocks from LDS (two 16-byte
-// granules each: K offsets c0 and c1 of the step), then 16 scaled MFMAs with
-// scale byte OPSEL of each lane's scale dword.
+// Scale dwords of one 256-wide chunk into LDS buffer `par`: the tile's 8 A
+// and 8 B 32-row units (256 bytes = one dword per lane each); this wave
+// loads units 2w and 2w + 1 of both.  sbase/tbase are the packed scale
+// arrays at the chunk, soff/toff this lane's offsets for the two units.
+constexpr int kScaleDma = 4;  // vector-memory instructions per wave per chunk
+__device__ __forceinline__ void issue_scales(const uint8_t* sbase, const uint8_t* tbase, const uint32_t (&soff)[2],
+                                             const uint32_t (&toff)[2], int par, int w) {
+    const uint8_t* sb = uniform_ptr(sbase);
+    const uint8_t* tb = uniform_ptr(tbase);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        dma4(sb, soff[u], __builtin_amdgcn_readfirstlane(lds_addr((const uint8_t*)lds_sa[par][2 * w + u])));
+        dma4(tb, toff[u], __builtin_amdgcn_readfirstlane(lds_addr((const uint8_t*)lds_sb[par][2 * w + u])));
+    }
+}
+
+// One 64-wide K step from LDS buffer `buf`: fragments of 4 A and 4 B blocks
+// (granules h and 2 + h of each lane's row: bytes 0-15 of every lane are the
+// instruction's first 32-wide K block, bytes 16-31 its second), then 16
+// scaled MFMAs using byte OPSEL of each lane's scale dword.
 template <int OPSEL>
-__device__ __forceinline__ void compute_step(const uint8_t* la, const uint8_t* lb, const int (&aoff)[4],
-                                             const int (&boff)[4], int c0, int c1, const uint32_t (&sa)[4],
-                                             const uint32_t (&sb)[4], f32x16 (&acc)[4][4]) {
+__device__ __forceinline__ void compute_step(int buf, const int (&aoff)[4], const int (&boff)[4], const int (&g0)[4],
+                                             const int (&g1)[4], const uint32_t (&sa)[4], const uint32_t (&sb)[4],
+                                             f32x16 (&acc)[4][4]) {
+    const uint8_t* la = lds_a[buf];
+    const uint8_t* lb = lds_b[buf];
     i32x8 af[4], bf[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(la + aoff[i] + c0);
-        const uint4 hi = *reinterpret_cast<const uint4*>(la + aoff[i] + c1);
+        const uint4 lo = *reinterpret_cast<const uint4*>(la + aoff[i] + g0[i]);
+        const uint4 hi = *reinterpret_cast<const uint4*>(la + aoff[i] + g1[i]);
         af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(lb + boff[j] + c0);
-        const uint4 hi = *reinterpret_cast<const uint4*>(lb + boff[j] + c1);
+        const uint4 lo = *reinterpret_cast<const uint4*>(lb + boff[j] + g0[j]);
+        const uint4 hi = *reinterpret_cast<const uint4*>(lb + boff[j] + g1[j]);
         bf[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
 #pragma unroll
@@ -157,57 +195,51 @@ __device__ __forceinline__ void compute_step(const uint8_t* la, const uint8_t* l
                                                                        (int)sa[i], OPSEL, (int)sb[j]);
 }
 
-// One 128-wide K stage = two steps, op_sel OPSEL0 and OPSEL0 + 1.
-template <int OPSEL0>
-__device__ __forceinline__ void compute_stage(const uint8_t* la, const uint8_t* lb, const int (&aoff)[4],
-                                              const int (&boff)[4], int x00, int x01, int x10, int x11,
-                                              const uint32_t (&sa)[4], const uint32_t (&sb)[4],
-                                              f32x16 (&acc)[4][4]) {
-    compute_step<OPSEL0>(la, lb, aoff, boff, x00, x01, sa, sb, acc);
-    compute_step<OPSEL0 + 1>(la, lb, aoff, boff, x10, x11, sa, sb, acc);
-}
-
-__device__ __forceinline__ void run_tile_impl(const Tile& T, uint8_t* __restrict__ la0, uint8_t* __restrict__ la1,
-                                              uint8_t* __restrict__ lb0, uint8_t* __restrict__ lb1) {
+__device__ __forceinline__ void run_tile_impl(const Tile& T) {
     const int t = threadIdx.x;
     const int w = t >> 6;
     const int l = t & 63;
     const int wm = w >> 1, wn = w & 1;
     const int h = l >> 5, r32 = l & 31;
 
-    // Tile bases (uniform) and per-lane 32-bit row offsets.  Rows past the
-    // operand's limit read its last row instead; their results are dropped.
+    // Tile bases (uniform) and per-lane 32-bit row offsets for the DMA.
+    // Rows past the operand's limit read its last row instead; their
+    // results are dropped by the epilogue.
     const uint8_t* abase = T.A + T.a_row0 * T.lda;
     const uint8_t* bbase = T.B + T.b_row0 * T.ldb;
-    uint32_t aoffs[8], boffs[8];
+    uint32_t aoffs[4], boffs[4];
     {
-        const int gran = ((l & 7) ^ (l >> 3)) * 16;  // logical granule stored at physical l%8
         const int64_t alast = T.a_lim - 1 - T.a_row0, blast = T.b_lim - 1 - T.b_row0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t rr = w * 64 + j * 8 + (l >> 3);
+        for (int j = 0; j < 4; ++j) {
+            const int rr = w * 64 + j * 16 + (l >> 2);        // tile row written by this lane
+            const int gran = ((l & 3) ^ swz(rr)) * 16;       // logical granule stored at physical l%4
             aoffs[j] = (uint32_t)((rr < alast ? rr : alast) * T.lda + gran);
             boffs[j] = (uint32_t)((rr < blast ? rr : blast) * T.ldb + gran);
         }
     }
-    // fragment offsets in LDS and granule offsets of the two 64-wide steps
-    int aoff[4], boff[4];
+    // fragment rows in LDS and the physical granules of this lane's two
+    // 16-byte pieces (logical granules h and 2 + h)
+    int aoff[4], boff[4], ga0[4], ga1[4], gb0[4], gb1[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        aoff[i] = (wm * 128 + i * 32 + r32) * TK;
-        boff[i] = (wn * 128 + i * 32 + r32) * TK;
+        const int ra = wm * 128 + i * 32 + r32, rb = wn * 128 + i * 32 + r32;
+        aoff[i] = ra * TK;
+        boff[i] = rb * TK;
+        ga0[i] = ((0 + h) ^ swz(ra)) * 16;
+        ga1[i] = ((2 + h) ^ swz(ra)) * 16;
+        gb0[i] = ((0 + h) ^ swz(rb)) * 16;
+        gb1[i] = ((2 + h) ^ swz(rb)) * 16;
     }
-    const int sw = r32 & 7;
-    const int x00 = ((0 + h) ^ sw) * 16, x01 = ((2 + h) ^ sw) * 16;
-    const int x10 = ((4 + h) ^ sw) * 16, x11 = ((6 + h) ^ sw) * 16;
-    // scale dword offsets (chunk 0) from the packed arrays' bases
-    uint32_t saoff[4], sboff[4];
+    // scale offsets (chunk 0) of this lane for the units 2w, 2w + 1 it loads:
+    // lane l carries row 32 u + l % 32 and K-block half l / 32
+    uint32_t soff[2], toff[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t ra = clamp64(T.a_row0 + wm * 128 + i * 32 + r32, 0, T.a_lim - 1);
-        const int64_t rb = clamp64(T.b_row0 + wn * 128 + i * 32 + r32, 0, T.b_lim - 1);
-        saoff[i] = (uint32_t)((ra >> 5) * T.a_unit + 4 * (32 * h + (ra & 31)));
-        sboff[i] = (uint32_t)((rb >> 5) * T.b_unit + 4 * (32 * h + (rb & 31)));
+    for (int u = 0; u < 2; ++u) {
+        const int64_t ra = clamp64(T.a_row0 + (2 * w + u) * 32 + r32, 0, T.a_lim - 1);
+        const int64_t rb = clamp64(T.b_row0 + (2 * w + u) * 32 + r32, 0, T.b_lim - 1);
+        soff[u] = (uint32_t)((ra >> 5) * T.a_unit + 4 * (32 * h + (ra & 31)));
+        toff[u] = (uint32_t)((rb >> 5) * T.b_unit + 4 * (32 * h + (rb & 31)));
     }
 
     f32x16 acc[4][4];
@@ -220,42 +252,64 @@ __device__ __forceinline__ void run_tile_impl(const Tile& T, uint8_t* __restrict
 
     const int64_t nchunk = (T.k1 - T.k0) / 256;
     if (nchunk > 0) {
-        uint32_t sa[4], sb[4], na[4], nb[4];
+        // Pipeline (stage j = K bytes [k0 + 64 j, k0 + 64 j + 64), buffer j % 4;
+        // scales of chunk c in LDS buffer c % 2):
+        //   prologue: scales(0), stages 0, 1, 2
+        //   chunk c, step s (stage 4c + s): wait for stage 4c + s; barrier;
+        //     issue stage 4c + s + 3 (at s = 0 followed by scales(c + 1));
+        //     multiply stage 4c + s with op_sel s.
+        // Vector-memory operations issued after stage 4c + s, i.e. the vmcnt
+        // bound of its wait: two stages at s = 0; two stages and one scale
+        // group at s = 1, 2, 3.  The last chunk waits for everything.
         const uint8_t* As = T.As + (T.k0 / 256) * 256;
         const uint8_t* Bs = T.Bs + (T.k0 / 256) * 256;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            na[i] = *reinterpret_cast<const uint32_t*>(As + saoff[i]);
-            nb[i] = *reinterpret_cast<const uint32_t*>(Bs + sboff[i]);
-        }
-        issue_stage(abase + T.k0, bbase + T.k0, aoffs, boffs, la0, lb0, w);
+        const uint8_t* ak = abase + T.k0;
+        const uint8_t* bk = bbase + T.k0;
+        uint32_t sa[4], sb[4];
+        issue_scales(As, Bs, soff, toff, 0, w);
+        issue_stage(ak, bk, aoffs, boffs, 0, w);
+        issue_stage(ak + TK, bk + TK, aoffs, boffs, 1, w);
+        issue_stage(ak + 2 * TK, bk + 2 * TK, aoffs, boffs, 2, w);
+        constexpr int kWait0 = 2 * kDmaPerStage;
+        constexpr int kWait1 = 2 * kDmaPerStage + kScaleDma;
         for (int64_t c = 0; c < nchunk; ++c) {
-            const int64_t kc = T.k0 + c * 256;
-            // first half of the chunk: buffer 0, op_sel 0/1
-            wait_vmem_all();
+            const bool more = c + 1 < nchunk;
+            const int par = (int)(c & 1);
+            const uint8_t* akc = ak + c * 256;
+            const uint8_t* bkc = bk + c * 256;
+            // s = 0
+            if (more) wait_vm<kWait0>();
+            else wait_vm<0>();
             __syncthreads();
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                sa[i] = na[i];
-                sb[i] = nb[i];
+                sa[i] = lds_sa[par][wm * 4 + i][l];
+                sb[i] = lds_sb[par][wn * 4 + i][l];
             }
-            issue_stage(abase + kc + TK, bbase + kc + TK, aoffs, boffs, la1, lb1, w);
-            if (c + 1 < nchunk) {
-                As += 256;
-                Bs += 256;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    na[i] = *reinterpret_cast<const uint32_t*>(As + saoff[i]);
-                    nb[i] = *reinterpret_cast<const uint32_t*>(Bs + sboff[i]);
-                }
-            }
-            compute_stage<0>(la0, lb0, aoff, boff, x00, x01, x10, x11, sa, sb, acc);
+            issue_stage(akc + 3 * TK, bkc + 3 * TK, aoffs, boffs, 3, w);
+            if (more) issue_scales(As + (c + 1) * 256, Bs + (c + 1) * 256, soff, toff, par ^ 1, w);
+            compute_step<0>(0, aoff, boff, ga0, ga1, sa, sb, acc);
             pin_acc(acc);
-            // second half: buffer 1, op_sel 2/3
-            wait_vmem_all();
+            // s = 1
+            if (more) wait_vm<kWait1>();
+            else wait_vm<0>();
             __syncthreads();
-            if (c + 1 < nchunk) issue_stage(abase + kc + 256, bbase + kc + 256, aoffs, boffs, la0, lb0, w);
-            compute_stage<2>(la1, lb1, aoff, boff, x00, x01, x10, x11, sa, sb, acc);
+            if (more) issue_stage(akc + 4 * TK, bkc + 4 * TK, aoffs, boffs, 0, w);
+            compute_step<1>(1, aoff, boff, ga0, ga1, sa, sb, acc);
+            pin_acc(acc);
+            // s = 2
+            if (more) wait_vm<kWait1>();
+            else wait_vm<0>();
+            __syncthreads();
+            if (more) issue_stage(akc + 5 * TK, bkc + 5 * TK, aoffs, boffs, 1, w);
+            compute_step<2>(2, aoff, boff, ga0, ga1, sa, sb, acc);
+            pin_acc(acc);
+            // s = 3
+            if (more) wait_vm<kWait1>();
+            else wait_vm<0>();
+            __syncthreads();
+            if (more) issue_stage(akc + 6 * TK, bkc + 6 * TK, aoffs, boffs, 2, w);
+            compute_step<3>(3, aoff, boff, ga0, ga1, sa, sb, acc);
             pin_acc(acc);
         }
     }
@@ -288,7 +342,7 @@ __device__ __forceinline__ void run_tile_impl(const Tile& T, uint8_t* __restrict
     __syncthreads();
 }
 
-__device__ __forceinline__ void run_tile(const Tile& T) { run_tile_impl(T, lds_a0, lds_a1, lds_b0, lds_b1); }
+__device__ __forceinline__ void run_tile(const Tile& T) { run_tile_impl(T); }
 
 __device__ __forceinline__ int64_t group_lo(const int32_t* off, int g, int64_t M) {
     return clamp64(off[g], 0, M);

@@ -10,6 +10,18 @@ typedef short i16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Streaming (non-temporal) 16-byte load / 8-byte store: the quantize
+// kernels touch every byte exactly once.
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream8(void* p, uint2 v) {
+    __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(p));
+}
 
 // Largest group count accepted by the grouped entry points.
 constexpr int kMaxGroups = 4096;

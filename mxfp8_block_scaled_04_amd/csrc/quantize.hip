@@ -12,19 +12,28 @@
 namespace mx {
 
 // ---------------------------------------------------------------------------
-// Row-wise.  One workgroup (4 waves) quantizes one unit of 32 rows x 256
-// columns: each wave covers 8 rows with four 16-byte loads per lane (lanes
-// 0-31 one row, 32-63 the next; 4 lanes per 32-wide block).  The block max is
+// Row-wise.  One workgroup of kRowsWaves waves quantizes one unit of 32 rows
+// x 256 columns (16 KB of bf16): every load instruction covers two rows
+// (lanes 0-31 one row, 32-63 the next; 4 lanes per 32-wide block), so each
+// lane issues 16 / kRowsWaves 16-byte loads -- short-lived lanes with one or
+// two loads in flight stream HBM best on this part.  The block max is
 // reduced over the lane quad with DPP, the codes are stored 8 bytes per lane
 // (256 contiguous bytes per row), and the unit's 256 scale bytes are staged
 // in LDS in packed order and written as one coalesced 256-byte store.
 // Rows >= M and blocks >= K read as zero, which yields scale 0 and keeps the
 // pad bytes of the packed scale array at 0.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __restrict__ x, int64_t M,
-                                                            int64_t K, int64_t ldx,
-                                                            uint8_t* __restrict__ q,
-                                                            uint8_t* __restrict__ s, int64_t nchunks) {
+#ifndef MX_ROWS_WAVES
+#define MX_ROWS_WAVES 8
+#endif
+constexpr int kRowsWaves = MX_ROWS_WAVES;
+constexpr int kRowsLoads = 16 / kRowsWaves;  // 16-byte loads per lane
+static_assert(kRowsWaves == 4 || kRowsWaves == 8 || kRowsWaves == 16, "unit = 32 rows");
+
+__global__ __launch_bounds__(64 * kRowsWaves) void quantize_rows_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                                        int64_t K, int64_t ldx,
+                                                                        uint8_t* __restrict__ q,
+                                                                        uint8_t* __restrict__ s, int64_t nchunks) {
     __shared__ uint32_t unit_s[64];
     const int t = threadIdx.x;
     const int w = t >> 6;
@@ -34,27 +43,27 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __re
     const int64_t col = ch * 256 + (l & 31) * 8;
     const bool colok = col < K;  // K % 32 == 0: a lane's 8 columns are all in or all out
 
-    uint4 d[4];
+    uint4 d[kRowsLoads];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t row = ru * 32 + w * 8 + 2 * i + (l >> 5);
+    for (int i = 0; i < kRowsLoads; ++i) {
+        const int64_t row = ru * 32 + w * (2 * kRowsLoads) + 2 * i + (l >> 5);
         d[i] = make_uint4(0, 0, 0, 0);
-        if (colok && row < M) d[i] = *reinterpret_cast<const uint4*>(x + row * ldx + col);
+        if (colok && row < M) d[i] = load_stream16(x + row * ldx + col);
     }
     uint8_t* us = reinterpret_cast<uint8_t*>(unit_s);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r32 = w * 8 + 2 * i + (l >> 5);
+    for (int i = 0; i < kRowsLoads; ++i) {
+        const int r32 = w * (2 * kRowsLoads) + 2 * i + (l >> 5);
         const int64_t row = ru * 32 + r32;
         const uint32_t S = scale_from_maxmag(quad_max_u32(max_mag8(d[i])));
         const uint2 c = quant8(d[i], S);
-        if (colok && row < M) *reinterpret_cast<uint2*>(q + row * K + col) = c;
+        if (colok && row < M) store_stream8(q + row * K + col, c);
         if ((l & 3) == 0) us[unit_byte((uint32_t)r32, (uint32_t)((l & 31) >> 2))] = (uint8_t)S;
     }
     __syncthreads();
     if (t < 64) {
         const int64_t KB = nchunks * 8;
-        reinterpret_cast<uint32_t*>(s + ru * 32 * KB + ch * 256)[t] = unit_s[t];
+        __builtin_nontemporal_store(unit_s[t], reinterpret_cast<uint32_t*>(s + ru * 32 * KB + ch * 256) + t);
     }
 }
 
@@ -63,8 +72,8 @@ hipError_t launch_quantize_rows(const uint16_t* x, int64_t M, int64_t K, int64_t
     if (M == 0 || K == 0) return hipSuccess;
     const int64_t nchunks = (K + 255) / 256;
     const int64_t units = ((M + 31) / 32) * nchunks;
-    hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)units), dim3(256), 0, stream, x, M, K, ldx, q, s,
-                       nchunks);
+    hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)units), dim3(64 * kRowsWaves), 0, stream, x, M, K,
+                       ldx, q, s, nchunks);
     return hipGetLastError();
 }
 
@@ -118,23 +127,34 @@ __global__ __launch_bounds__(1024) void cols_prefix_kernel(const int32_t* __rest
     if (t == 1023 && G == 4 * 1024) P[G] = run;  // the one entry past every slice
 }
 
-// One workgroup (4 waves) handles padded column tile pt (256 rows of one
-// group) x 64 columns of x.  Load: each lane reads 16 bytes (8 columns) of
-// two adjacent rows and pairs them per column with v_perm into dwords
-// (x[m][n], x[m+1][n]), stored transposed in LDS with a 16-byte XOR swizzle.
-// Compute: each lane reads 16 bytes = 8 consecutive rows of one column,
-// 4 lanes per 32-row block, and proceeds as the row-wise kernel.
-__global__ __launch_bounds__(256) void quantize_cols_kernel(const uint16_t* __restrict__ x, int64_t M,
-                                                            int64_t N, int64_t ldx,
-                                                            const int32_t* __restrict__ off,
-                                                            const int32_t* __restrict__ P, int32_t G,
-                                                            uint8_t* __restrict__ qT,
-                                                            uint8_t* __restrict__ sT, int64_t Mcap) {
+// One workgroup handles padded column tile pt (256 rows of one group) x 64
+// columns of x.  Load: each task reads 16 bytes (8 columns) of two adjacent
+// rows and pairs them per column with v_perm into dwords (x[m][n],
+// x[m+1][n]), stored transposed in LDS with a 16-byte XOR swizzle (writes
+// spread over all banks, reads of 16 contiguous bytes conflict-free).
+// Compute: each task reads 16 bytes = 8 consecutive rows of one column,
+// 4 lanes per 32-row block, and proceeds as the row-wise kernel; lanes 0-31
+// of a wave store 256 contiguous code bytes of one transposed row.
+#ifndef MX_COLS_THREADS
+#define MX_COLS_THREADS 256
+#endif
+constexpr int kColsThreads = MX_COLS_THREADS;
+static_assert(kColsThreads == 256 || kColsThreads == 512 || kColsThreads == 1024, "tile tasks");
+
+__global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                                     int64_t N, int64_t ldx,
+                                                                     const int32_t* __restrict__ off,
+                                                                     const int32_t* __restrict__ P, int32_t G,
+                                                                     uint8_t* __restrict__ qT,
+                                                                     uint8_t* __restrict__ sT, int64_t Mcap) {
     // tile[n][pair]: 64 columns x 128 row pairs, 16-byte granules swizzled by n/8
     __shared__ uint4 tile[64 * 32];
     __shared__ uint32_t unit_s[2][64];
     __shared__ int32_t sh_g;
     const int t = threadIdx.x;
+    // row tiles vary fastest: workgroups dispatched together read far-apart
+    // rows (spread over all HBM channels) and write adjacent 256-byte pieces
+    // of the same transposed rows
     const int64_t pt = blockIdx.x;
     const int64_t nt = blockIdx.y;
     const int64_t col0 = pt * 256;  // padded column of the transposed result
@@ -145,7 +165,7 @@ __global__ __launch_bounds__(256) void quantize_cols_kernel(const uint16_t* __re
     if (off == nullptr) {
         if (col0 < ((M + 255) / 256) * 256 && t == 0) sh_g = 0;
     } else {
-        for (int g = t; g < G; g += 256)
+        for (int g = t; g < G; g += kColsThreads)
             if (P[g] <= col0 && col0 < P[g + 1]) sh_g = g;
     }
     __syncthreads();
@@ -160,17 +180,17 @@ __global__ __launch_bounds__(256) void quantize_cols_kernel(const uint16_t* __re
             row_end = o1;
         }
     }
-    // ---- load + transpose into LDS
+    // ---- load + transpose into LDS (1024 pair tasks)
     const int c8 = t & 7;  // 16-byte column chunk (8 columns)
     const int64_t ncol = nt * 64 + c8 * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int pr = i * 32 + (t >> 3);  // row pair 0..127
+    for (int i = 0; i < 1024 / kColsThreads; ++i) {
+        const int pr = i * (kColsThreads / 8) + (t >> 3);  // row pair 0..127
         const int64_t r0 = row_begin + 2 * pr, r1 = r0 + 1;
         uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
         if (g >= 0 && ncol < N) {
-            if (r0 < row_end) a = *reinterpret_cast<const uint4*>(x + r0 * ldx + ncol);
-            if (r1 < row_end) b = *reinterpret_cast<const uint4*>(x + r1 * ldx + ncol);
+            if (r0 < row_end) a = load_stream16(x + r0 * ldx + ncol);
+            if (r1 < row_end) b = load_stream16(x + r1 * ldx + ncol);
         }
         const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
         const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
@@ -185,17 +205,17 @@ __global__ __launch_bounds__(256) void quantize_cols_kernel(const uint16_t* __re
         }
     }
     __syncthreads();
-    // ---- quantize 8 consecutive rows of one column per lane
+    // ---- quantize 8 consecutive rows of one column per task (2048 tasks)
     const int j = t & 31;  // granule: rows 8j..8j+7 of the tile, block j/4
     uint8_t* us = reinterpret_cast<uint8_t*>(unit_s);
-#pragma unroll 2
-    for (int i = 0; i < 8; ++i) {
-        const int n = i * 8 + (t >> 5);
+#pragma unroll
+    for (int i = 0; i < 2048 / kColsThreads; ++i) {
+        const int n = i * (kColsThreads / 32) + (t >> 5);
         const uint4 d = tile[n * 32 + (j ^ ((n >> 3) & 7))];
         const uint32_t S = scale_from_maxmag(quad_max_u32(max_mag8(d)));
         const uint2 c = quant8(d, S);
         const int64_t ng = nt * 64 + n;
-        if (ng < N) *reinterpret_cast<uint2*>(qT + ng * Mcap + col0 + 8 * j) = c;
+        if (ng < N) store_stream8(qT + ng * Mcap + col0 + 8 * j, c);
         if ((t & 3) == 0) us[(n >> 5) * 256 + unit_byte((uint32_t)(n & 31), (uint32_t)(j >> 2))] = (uint8_t)S;
     }
     __syncthreads();
@@ -204,7 +224,8 @@ __global__ __launch_bounds__(256) void quantize_cols_kernel(const uint16_t* __re
         const int64_t rowunit = nt * 2 + u;
         if (rowunit * 32 < N) {
             const int64_t KB = Mcap / 32;
-            reinterpret_cast<uint32_t*>(sT + rowunit * 32 * KB + pt * 256)[t & 63] = unit_s[u][t & 63];
+            __builtin_nontemporal_store(unit_s[u][t & 63],
+                                        reinterpret_cast<uint32_t*>(sT + rowunit * 32 * KB + pt * 256) + (t & 63));
         }
     }
 }
@@ -222,7 +243,7 @@ hipError_t launch_quantize_cols(const uint16_t* x, int64_t M, int64_t N, int64_t
     }
     if (N == 0 || Mcap == 0) return hipSuccess;
     dim3 grid((unsigned)(Mcap / 256), (unsigned)((N + 63) / 64));
-    hipLaunchKernelGGL(quantize_cols_kernel, grid, dim3(256), 0, stream, x, M, N, ldx, group_offsets,
+    hipLaunchKernelGGL(quantize_cols_kernel, grid, dim3(kColsThreads), 0, stream, x, M, N, ldx, group_offsets,
                        (const int32_t*)padded_offsets, G, qT, sT, Mcap);
     return hipGetLastError();
 }
