@@ -235,8 +235,11 @@ __device__ __forceinline__ void mfma_step(Frags& F, const uint32_t (&sa)[4], con
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.a[i], F.b[j], acc[i][j], 0, 0, OPSEL,
-                                                                       (int)sa[i], OPSEL, (int)sb[j]);
+            // B (weight) rows as the instruction's rows and A (token) rows as its
+            // columns: each lane then holds 4 consecutive output columns of one
+            // output row (see the epilogue)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[j], F.a[i], acc[i][j], 0, 0, OPSEL,
+                                                                       (int)sb[j], OPSEL, (int)sa[i]);
         i32x8& nxt = F.a[i < 3 ? i + 1 : i];
         if (i < 2) {
             dma16_between(ab, aoffs[2 * i], a0 + (2 * i) * 16 * TK, F.a[i], nxt);
@@ -387,28 +390,40 @@ __device__ __forceinline__ void run_tile_impl(const Tile& T) {
             }
         }
     }
-    // epilogue: lane holds column r32 of each 32 x 32 block, rows
-    // 8*(e/4) + 4*h + e%4.  The lane bases are made opaque here so that the
-    // compiler does not hoist all 256 row/address values out of the
-    // persistent tile loop (which would not fit in registers).
-    int rb = wm * 128 + 4 * h;
-    int cb = wn * 128 + r32;
+    // Epilogue.  acc[i][j] is the 32 x 32 block (A rows 32 i.., B rows 32 j..)
+    // of this wave's 128 x 128 share, transposed by the operand order above:
+    // lane l holds output row 32 i + l % 32 and, in element 4 q + u, output
+    // column 32 j + 8 q + 4 (l / 32) + u -- four consecutive bf16 columns,
+    // stored as one 8-byte write when the row pitch allows it.  The lane bases
+    // are made opaque here so that the compiler does not hoist all the
+    // row/address values out of the persistent tile loop.
+    int rb = wm * 128 + r32;
+    int cb = wn * 128 + 4 * h;
     uint32_t ldo = (uint32_t)T.ldo;
     asm volatile("" : "+v"(rb), "+v"(cb), "+s"(ldo));
-    uint16_t* const o = T.out;
+    const bool vec = (ldo & 3) == 0 && (((uintptr_t)T.out) & 7) == 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int col = cb + j * 32;
-        if (col >= T.cols) continue;
-        uint16_t* const oc = o + col;
+    for (int i = 0; i < 4; ++i) {
+        const int row = rb + i * 32;
+        if (row >= T.rows) continue;
+        uint16_t* const orow = T.out + (uint32_t)row * ldo;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = rb + i * 32 + 8 * (e >> 2) + (e & 3);
-                if (row < T.rows) {
-                    const __bf16 v = (__bf16)acc[i][j][e];
-                    oc[(uint32_t)row * ldo] = __builtin_bit_cast(uint16_t, v);
+            for (int q = 0; q < 4; ++q) {
+                const int col = cb + j * 32 + q * 8;
+                const __bf16 b0 = (__bf16)acc[i][j][4 * q + 0], b1 = (__bf16)acc[i][j][4 * q + 1];
+                const __bf16 b2 = (__bf16)acc[i][j][4 * q + 2], b3 = (__bf16)acc[i][j][4 * q + 3];
+                if (vec && col + 4 <= T.cols) {
+                    const uint2 pk = make_uint2(
+                        (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16),
+                        (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16));
+                    *reinterpret_cast<uint2*>(orow + col) = pk;
+                } else {
+                    if (col + 0 < T.cols) orow[col + 0] = __builtin_bit_cast(uint16_t, b0);
+                    if (col + 1 < T.cols) orow[col + 1] = __builtin_bit_cast(uint16_t, b1);
+                    if (col + 2 < T.cols) orow[col + 2] = __builtin_bit_cast(uint16_t, b2);
+                    if (col + 3 < T.cols) orow[col + 3] = __builtin_bit_cast(uint16_t, b3);
                 }
             }
     }
