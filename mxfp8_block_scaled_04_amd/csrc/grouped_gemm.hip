@@ -10,20 +10,29 @@
 // written by the quantize kernels hands each lane that byte for four
 // consecutive 64-wide K steps in one dword (byte = op_sel).
 //
-// Kernel: persistent workgroups of 4 waves, tile 256 x 256, K stage 128.
-//  * fp8 A/B stages go straight from global memory into LDS with 16-byte
-//    global_load_lds (no VGPR staging), two buffers, one stage in flight
-//    while the previous one is multiplied.  Rows are stored 128 bytes apart
-//    with the 16-byte granule index XORed by (row mod 8), so the fragment
-//    reads (32 rows, same K offset) hit distinct banks.
+// Kernel: persistent workgroups of 4 waves, tile 256 x 256.
 //  * Each wave owns a 128 x 128 sub-tile = 4 x 4 MFMA blocks; per 64-wide K
-//    step a lane holds 16 bytes of each 32-wide block for its row.
-//  * Scale dwords come straight from global memory into VGPRs, one chunk
-//    (256 of K) ahead.
+//    step a lane holds 16 bytes of each 32-wide K block for its row.
+//  * fp8 operands reach LDS by direct buffer-to-LDS loads (no VGPR staging)
+//    in stages of 128 K bytes: every load instruction moves 8 whole 128-byte
+//    row segments (measured: 64-byte row pieces, 16 rows per instruction,
+//    cost ~11% of the matrix throughput; full 128-byte lines cost nothing
+//    measurable).  Two stage buffers (2 x 64 KB); the loads of stage s + 1
+//    are issued during the second K step of stage s - 1, and one barrier per
+//    stage both publishes a landed stage and frees the other buffer.
+//  * Loads go through buffer descriptors whose range ends at the tile's
+//    last valid row, so rows past a group's end read as zeros without any
+//    per-lane clamping, and the per-lane offsets do not depend on the tile.
+//  * The pipeline does not restart between tiles: the last chunk of a tile
+//    already loads the next tile's first two stages and scales, and the
+//    epilogue (bf16 conversion and 16-byte range-checked stores) runs while
+//    they are in flight.
+//  * Scale dwords go to LDS by the same direct loads, one 256-wide K chunk
+//    ahead, and are read into registers once per chunk.
 //  * Tile order: expert-major; inside an expert, bands of 4 M-tiles walked
-//    M-fastest; workgroups are mapped so that each XCD (workgroups are
-//    dealt to the 8 XCDs round-robin) runs a contiguous range of tile ids
-//    and so shares operands through its own L2.
+//    M-fastest; workgroups are mapped so that each XCD (workgroups are dealt
+//    to the 8 XCDs round-robin) runs a contiguous range of tile ids and so
+//    shares operands through its own L2.
 #include "mx_device.h"
 #include "mx_internal.h"
 
@@ -33,11 +42,12 @@ namespace {
 
 constexpr int TM = 256;
 constexpr int TN = 256;
-constexpr int TK = 64;     // K bytes per pipeline stage (one MFMA K step)
-constexpr int NBUF = 4;    // LDS stage buffers; three stages in flight
+constexpr int TK = 64;     // K bytes per MFMA step
+constexpr int SK = 128;    // K bytes per LDS stage (two MFMA steps)
 constexpr int kBand = 4;   // M-tiles per band of the tile order
 
 typedef __attribute__((address_space(3))) void lds_t;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 struct GemmArgs {
     const uint8_t* A;
@@ -47,29 +57,32 @@ struct GemmArgs {
     const int32_t* offsets;
     uint16_t* out;
     int64_t M, N, K, Mcap;
+    int64_t a_scale_bytes, b_scale_bytes;  // sizes of the packed scale arrays
     int32_t G;
     int32_t mode;  // 0: rows of X grouped (forward); 1: contraction grouped (wgrad);
                    // 2: rows grouped, weights read transposed (dgrad)
-    int64_t ldb;   // mode 2: row stride of the transposed weights (their Mcap)
+    int64_t ldb;   // mode 2: row stride of the transposed weights (their Wcap)
 };
 
+// Launch-wide constants of the operand layouts.
+struct Layout {
+    uint32_t lda, ldb;        // row strides (bytes) of the A and B data
+    uint32_t a_unit, b_unit;  // bytes per 32-row unit of the packed scales
+    uint32_t ldo;             // output row stride (elements)
+};
+
+// One output tile (all fields wave-uniform).
 struct Tile {
-    const uint8_t* A;   // base of A data (row 0)
-    const uint8_t* As;  // base of A packed scales (row 0)
-    int64_t lda, a_unit;  // row stride of A data; bytes per 32-row scale unit (32 * KB)
-    int64_t a_row0, a_lim;
-    const uint8_t* B;
-    const uint8_t* Bs;
-    int64_t ldb, b_unit;
-    int64_t b_row0, b_lim;
-    int64_t k0, k1;  // contraction range, multiples of 256
-    uint16_t* out;   // element (0, 0) of the tile
-    int64_t ldo;
-    int32_t rows, cols;  // valid part of the tile
+    i32x4 ra, rb;    // A / B data descriptors: base at the tile's first row and first contraction byte
+    i32x4 rsa, rsb;  // A / B packed-scale descriptors: base at the tile's first unit and chunk
+    int32_t asub, bsub;  // first tile row modulo 32 (A, B)
+    int32_t nchunk;      // 256-wide contraction chunks (0: no tile)
+    int32_t rows, cols;  // valid part of the output tile
+    uint16_t* out;       // output element (0, 0) of the tile
 };
 
-__shared__ __attribute__((aligned(16))) uint8_t lds_a[NBUF][TM * TK];
-__shared__ __attribute__((aligned(16))) uint8_t lds_b[NBUF][TN * TK];
+__shared__ __attribute__((aligned(16))) uint8_t lds_a[2][TM * SK];
+__shared__ __attribute__((aligned(16))) uint8_t lds_b[2][TN * SK];
 __shared__ __attribute__((aligned(16))) uint32_t lds_sa[2][TM / 32][64];  // scale dwords, [chunk parity][32-row unit][lane]
 __shared__ __attribute__((aligned(16))) uint32_t lds_sb[2][TN / 32][64];
 __shared__ int32_t tile_end[kMaxGroups];  // inclusive prefix of tiles per group
@@ -78,52 +91,85 @@ __device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
     return v < lo ? lo : (v > hi ? hi : v);
 }
 
-// Stage rows are 64 bytes (4 granules of 16 B).  Granule c of tile row r is
+// Stage rows are 128 bytes (8 granules of 16 B).  Granule c of tile row r is
 // stored at position c ^ swz(r).  Measured on gfx950: a 64-lane ds_read_b128
-// is served in 4 passes of 16 lanes at 256 bytes per clock, a pass taking
-// lanes whose row index varies in bits 0, 1, 3 and in bit 2 tied to bit 4.
-// With 64-byte rows the 16-byte bank group of a read is 4 (r mod 4) + granule,
-// so XORing the granule with bits 2-3 of the row makes the 16 groups of every
-// pass distinct (zero bank-conflict cycles measured for this pattern).
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+// is served in 4 passes of 16 lanes (256 bytes per clock), the lanes of a
+// pass having row indices that differ in bits 0, 1, 3 and in bit 2 tied to
+// bit 4.  With 128-byte rows the 16-byte bank group of a read is
+// 8 (r mod 2) + physical granule; XORing the granule with row bits 1-3 makes
+// the 16 groups of every pass distinct.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
-// The address base must be wave-uniform (an SGPR pair).
-__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
-    const uint64_t v = (uint64_t)(uintptr_t)p;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Raw buffer descriptor over [base, base + bytes): loads past the range
+// return zeros, stores past it are dropped (checked on the full offset,
+// including the scalar offset).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    i32x4 r;
+    r[0] = (int)uni((uint32_t)p);
+    r[1] = (int)uni((uint32_t)(p >> 32) & 0xFFFFu);  // stride 0, no swizzle
+    r[2] = (int)uni(bytes);
+    r[3] = (int)uni(0x00020000u);
+    return r;
 }
 
-// 16-byte direct global->LDS load (global_load_lds_dwordx4): lane i of the
-// wave writes LDS bytes [lds + 16 i, lds + 16 i + 16).  Issued as inline asm
-// so that the compiler's own wait insertion does not stall every later LDS
-// read on it; completion is enforced explicitly (wait_vm<N> + barrier)
-// before a buffer is read.  M0 is only written here; no other code in these
-// kernels reads it.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_t*)p; }
+
+// Direct buffer->LDS loads.  Issued as inline asm so that the compiler's own
+// wait insertion does not stall every later LDS read on them; completion is
+// enforced explicitly (wait_vm<N> + barrier) before a buffer is read.  M0 is
+// only written here; nothing else in these kernels reads it.
+//
+// bdma16: 16 bytes per lane (lane i writes LDS [lds + 16 i, lds + 16 i + 16)).
+// The asm claims to rewrite the A fragments `before` (read by the MFMAs that
+// must be issued first) and `after` (read by the MFMAs that must follow);
+// the registers are not touched, the claim only fixes the issue order so
+// that the load issue happens while the matrix pipe is busy.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds)
+// The scalar offset `so` and LDS address `lb` advance by `ld8` (8 rows) and
+// 8 * 128 bytes after every load, inside the asm, so that the compiler does
+// not precompute and hold the 8 offsets of a stage in scalar registers.
+__device__ __forceinline__ void bdma16_run(const i32x4& rs, uint32_t voff, uint32_t& so, uint32_t& lb, uint32_t ld8,
+                                           i32x8& before, i32x8& after) {
+    asm volatile(
+        "s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %4, %5, %2 offen lds\n\t"
+        "s_add_u32 %2, %2, %6\n\ts_add_u32 %3, %3, 0x400"
+        : "+v"(before), "+v"(after), "+s"(so), "+s"(lb)
+        : "v"(voff), "s"(rs), "s"(ld8)
+        : "memory", "m0", "scc");
+}
+__device__ __forceinline__ void bdma16_run_after(const i32x4& rs, uint32_t voff, uint32_t& so, uint32_t& lb,
+                                                 uint32_t ld8, i32x8& before) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %3, %4, %1 offen lds\n\t"
+        "s_add_u32 %1, %1, %5\n\ts_add_u32 %2, %2, 0x400"
+        : "+v"(before), "+s"(so), "+s"(lb)
+        : "v"(voff), "s"(rs), "s"(ld8)
+        : "memory", "m0", "scc");
+}
+__device__ __forceinline__ void bdma16_plain(const i32x4& rs, uint32_t voff, uint32_t soff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rs),
+                 "s"(soff), "s"(lds)
                  : "memory", "m0");
 }
-// Same DMA, ordered against the MFMAs around it: the asm claims to rewrite the
-// A fragments `before` (read by the MFMAs that must be issued first) and
-// `after` (read by the MFMAs that must follow).  The registers are not
-// touched; the claim only fixes the issue order, so that the DMA issue
-// happens while the matrix pipe is busy.
-__device__ __forceinline__ void dma16_between(const uint8_t* base, uint32_t voff, uint32_t lds, i32x8& before,
-                                              i32x8& after) {
-    asm volatile("s_mov_b32 m0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3"
-                 : "+v"(before), "+v"(after)
-                 : "v"(voff), "s"(base), "s"(lds)
+// 4 bytes per lane (lane i writes LDS [lds + 4 i, lds + 4 i + 4)).
+__device__ __forceinline__ void bdma4(const i32x4& rs, uint32_t voff, uint32_t soff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rs),
+                 "s"(soff), "s"(lds)
                  : "memory", "m0");
 }
-
-// 4-byte variant (global_load_lds_dword): lane i writes [lds + 4 i, lds + 4 i + 4).
-__device__ __forceinline__ void dma4(const uint8_t* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "s"(lds)
-                 : "memory", "m0");
+// Ordering point with no instruction: keeps the LDS reads of an MFMA group
+// between its neighbours (memory clobber) and the groups in order (fake
+// fragment dependencies, as above).
+__device__ __forceinline__ void order_between(i32x8& before, i32x8& after) {
+    asm volatile("" : "+v"(before), "+v"(after) : : "memory");
+}
+// 16-byte range-checked store.
+__device__ __forceinline__ void bstore16(const i32x4& rs, uint32_t voff, uint32_t soff, i32x4 v) {
+    asm volatile("buffer_store_dwordx4 %0, %1, %2, %3 offen" ::"v"(v), "v"(voff), "s"(rs), "s"(soff) : "memory");
 }
 #pragma clang diagnostic pop
 
@@ -145,92 +191,90 @@ __device__ __forceinline__ void pin_acc(f32x16 (&acc)[4][4]) {
         for (int j = 0; j < 4; ++j) asm volatile("" ::"a"(acc[i][j]));
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) { return (uint32_t)(uintptr_t)(lds_t*)p; }
+// Per-lane constants of the load and read patterns (independent of the tile).
+struct Lane {
+    uint32_t va[2], vb[2];  // load offsets for instructions of even / odd index j
+    int fo[4];              // fragment read offsets (A lo, A hi, B lo, B hi) of K half 0
+};
 
-// Direct-to-LDS loads of one 64-wide K stage: this wave's 64 rows of A and
-// of B, 4 instructions each (16 rows x 64 bytes per instruction).  abase and
-// bbase are the (uniform) addresses of the tile's first rows at column k.
-constexpr int kDmaPerStage = 8;  // vector-memory instructions per wave per stage
-__device__ __forceinline__ void issue_stage(const uint8_t* abase, const uint8_t* bbase, const uint32_t (&aoffs)[4],
-                                            const uint32_t (&boffs)[4], int buf, int w) {
-    const uint32_t a0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_a[buf]) + w * 64 * TK);
-    const uint32_t b0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_b[buf]) + w * 64 * TK);
-    const uint8_t* ab = uniform_ptr(abase);
-    const uint8_t* bb = uniform_ptr(bbase);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(ab, aoffs[j], a0 + j * 16 * TK);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(bb, boffs[j], b0 + j * 16 * TK);
+// One stage = 128 K bytes of the tile's 256 A rows and 256 B rows.  Wave w
+// loads rows [64 w, 64 w + 64) of both, 8 instructions each; instruction j
+// covers rows 64 w + 8 j + l / 8, lane l holding physical granule l % 8.
+struct StageDma {
+    i32x4 ra, rb;
+    uint32_t soff;    // contraction byte of the stage
+    uint32_t la, lb;  // LDS addresses of this wave's first row in the target buffer
+};
+
+// Packed-scale loads of one 256-wide chunk: the tile's 8 A and 8 B 32-row
+// units (256 bytes = one dword per lane each); wave w loads units 2w, 2w + 1.
+// Lane l carries row 32 u + l % 32 (of the tile) and K-block half l / 32.
+__device__ __forceinline__ uint32_t scale_lane_off(int sub, int tr, int h, uint32_t unit) {
+    const int r = sub + tr;
+    return (uint32_t)(r >> 5) * unit + 4u * (uint32_t)(32 * h + (r & 31));
 }
 
-// Scale dwords of one 256-wide chunk into LDS buffer `par`: the tile's 8 A
-// and 8 B 32-row units (256 bytes = one dword per lane each); this wave
-// loads units 2w and 2w + 1 of both.  sbase/tbase are the packed scale
-// arrays at the chunk, soff/toff this lane's offsets for the two units.
-constexpr int kScaleDma = 4;  // vector-memory instructions per wave per chunk
-__device__ __forceinline__ void issue_scales(const uint8_t* sbase, const uint8_t* tbase, const uint32_t (&soff)[2],
-                                             const uint32_t (&toff)[2], int par, int w) {
-    const uint8_t* sb = uniform_ptr(sbase);
-    const uint8_t* tb = uniform_ptr(tbase);
+__device__ __forceinline__ void issue_scales(const i32x4& rsa, const i32x4& rsb, int asub, int bsub,
+                                             uint32_t choff, int par, int w, int l, const Layout& L) {
+    const int h = l >> 5, r32 = l & 31;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        dma4(sb, soff[u], __builtin_amdgcn_readfirstlane(lds_addr((const uint8_t*)lds_sa[par][2 * w + u])));
-        dma4(tb, toff[u], __builtin_amdgcn_readfirstlane(lds_addr((const uint8_t*)lds_sb[par][2 * w + u])));
+        const int tr = (2 * w + u) * 32 + r32;
+        bdma4(rsa, scale_lane_off(asub, tr, h, L.a_unit), choff, uni(lds_addr(lds_sa[par][2 * w + u])));
+        bdma4(rsb, scale_lane_off(bsub, tr, h, L.b_unit), choff, uni(lds_addr(lds_sb[par][2 * w + u])));
     }
 }
+constexpr int kStageDma = 16;  // vector-memory instructions per wave per stage
 
-// Fragments of one 64-wide K step for this wave: 4 A and 4 B blocks, each
-// lane holding 32 bytes of its row (granules h and 2 + h: bytes 0-15 of every
+__device__ __forceinline__ void issue_stage_plain(const StageDma& S, const Lane& Ln, const Layout& L) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bdma16_plain(S.ra, Ln.va[j & 1], S.soff + j * 8 * L.lda, S.la + j * 8 * SK);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bdma16_plain(S.rb, Ln.vb[j & 1], S.soff + j * 8 * L.ldb, S.lb + j * 8 * SK);
+}
+
+// Fragments of one 64-wide K step: 4 A and 4 B blocks, each lane holding 32
+// bytes of its row (granules h and 2 + h of the step: bytes 0-15 of every
 // lane are the instruction's first 32-wide K block, bytes 16-31 its second).
 struct Frags {
     i32x8 a[4], b[4];
 };
 
-__device__ __forceinline__ void read_frags(int buf, const int (&aoff)[4], const int (&boff)[4], const int (&ga0)[4],
-                                           const int (&ga1)[4], const int (&gb0)[4], const int (&gb1)[4], Frags& F) {
+__device__ __forceinline__ i32x8 lds_frag(const uint8_t* base, int lo, int hi) {
+    const uint4 x = *reinterpret_cast<const uint4*>(base + lo);
+    const uint4 y = *reinterpret_cast<const uint4*>(base + hi);
+    return i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+}
+
+// Fragment reads of K half `half` (0: stage bytes 0-63, 1: 64-127) of
+// buffer `buf`: granule g of half 1 is granule g + 4 of the row, i.e. the
+// physical offset XOR 64.
+__device__ __forceinline__ void read_frags(int buf, int half, const Lane& Ln, Frags& F) {
+    const int x = half ? 64 : 0;
     const uint8_t* la = lds_a[buf];
     const uint8_t* lb = lds_b[buf];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(la + aoff[i] + ga0[i]);
-        const uint4 hi = *reinterpret_cast<const uint4*>(la + aoff[i] + ga1[i]);
-        F.a[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
+    for (int i = 0; i < 4; ++i) F.a[i] = lds_frag(la + i * 32 * SK, Ln.fo[0] ^ x, Ln.fo[1] ^ x);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(lb + boff[j] + gb0[j]);
-        const uint4 hi = *reinterpret_cast<const uint4*>(lb + boff[j] + gb1[j]);
-        F.b[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
+    for (int j = 0; j < 4; ++j) F.b[j] = lds_frag(lb + j * 32 * SK, Ln.fo[2] ^ x, Ln.fo[3] ^ x);
 }
 
-// Ask the scheduler to interleave the next step's 16 fragment reads with the
-// first MFMAs of this step (4 reads, 1 MFMA, ...), so that the reads are in
-// flight early and done by the next barrier.
-__device__ __forceinline__ void interleave_reads_with_mfma() {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
-}
-
-// 16 scaled MFMAs of one K step, scale byte OPSEL of each lane's dwords, in
-// 4 groups (one A block each), with the 8 DMA instructions of a stage (A rows
-// of this wave's share, then B) issued two after each group, while the
-// matrix pipe works on that group.  The DMA is unconditional (no branch that
-// would let the compiler reorder the groups): at the end of the contraction
-// the caller points it at a stage that is already resident, reloading it
-// into the buffer that stage occupies.
-template <int OPSEL>
-__device__ __forceinline__ void mfma_step(Frags& F, const uint32_t (&sa)[4], const uint32_t (&sb)[4],
-                                          f32x16 (&acc)[4][4], const uint8_t* an, const uint8_t* bn, int nbuf,
-                                          const uint32_t (&aoffs)[4], const uint32_t (&boffs)[4], int w) {
-    const uint32_t a0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_a[nbuf]) + w * 64 * TK);
-    const uint32_t b0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_b[nbuf]) + w * 64 * TK);
-    const uint8_t* ab = uniform_ptr(an);
-    const uint8_t* bb = uniform_ptr(bn);
+// One 64-wide K step: 16 scaled MFMAs on the fragments F (scale byte OPSEL
+// of each lane's scale dwords), in 4 groups of one A block each.  After
+// group i the step reads block i of A and of B of the next step (buffer
+// rbuf, K half rhalf) into Fn, so that the four waves, which leave a barrier
+// together, do not all queue their 16 KB of LDS reads at once while the
+// matrix pipe idles.  With DMA, the step also issues the 16 loads of a stage
+// (4 after each group: A rows, then B rows) while the matrix pipe works on
+// that group; without, an empty ordering point keeps the same shape.
+template <int OPSEL, bool DMA>
+__device__ __forceinline__ void mfma_step(Frags& F, Frags& Fn, int rbuf, int rhalf, const Lane& Ln,
+                                          const uint32_t (&sa)[4], const uint32_t (&sb)[4], f32x16 (&acc)[4][4],
+                                          const StageDma& S, const Layout& L) {
+    const int x = rhalf ? 64 : 0;
+    const uint8_t* la = lds_a[rbuf];
+    const uint8_t* lb = lds_b[rbuf];
+    uint32_t soa = S.soff, sob = S.soff, lba = S.la, lbb = S.lb;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -240,214 +284,284 @@ __device__ __forceinline__ void mfma_step(Frags& F, const uint32_t (&sa)[4], con
             // output row (see the epilogue)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[j], F.a[i], acc[i][j], 0, 0, OPSEL,
                                                                        (int)sb[j], OPSEL, (int)sa[i]);
-        i32x8& nxt = F.a[i < 3 ? i + 1 : i];
-        if (i < 2) {
-            dma16_between(ab, aoffs[2 * i], a0 + (2 * i) * 16 * TK, F.a[i], nxt);
-            dma16_between(ab, aoffs[2 * i + 1], a0 + (2 * i + 1) * 16 * TK, F.a[i], nxt);
-        } else {
-            dma16_between(bb, boffs[2 * i - 4], b0 + (2 * i - 4) * 16 * TK, F.a[i], nxt);
-            dma16_between(bb, boffs[2 * i - 3], b0 + (2 * i - 3) * 16 * TK, F.a[i], nxt);
-        }
-    }
-}
-
-__device__ __forceinline__ void run_tile_impl(const Tile& T) {
-    const int t = threadIdx.x;
-    const int w = t >> 6;
-    const int l = t & 63;
-    const int wm = w >> 1, wn = w & 1;
-    const int h = l >> 5, r32 = l & 31;
-
-    // Tile bases (uniform) and per-lane 32-bit row offsets for the DMA.
-    // Rows past the operand's limit read its last row instead; their
-    // results are dropped by the epilogue.
-    const uint8_t* abase = T.A + T.a_row0 * T.lda;
-    const uint8_t* bbase = T.B + T.b_row0 * T.ldb;
-    uint32_t aoffs[4], boffs[4];
-    {
-        const int64_t alast = T.a_lim - 1 - T.a_row0, blast = T.b_lim - 1 - T.b_row0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int rr = w * 64 + j * 16 + (l >> 2);        // tile row written by this lane
-            const int gran = ((l & 3) ^ swz(rr)) * 16;       // logical granule stored at physical l%4
-            aoffs[j] = (uint32_t)((rr < alast ? rr : alast) * T.lda + gran);
-            boffs[j] = (uint32_t)((rr < blast ? rr : blast) * T.ldb + gran);
-        }
-    }
-    // fragment rows in LDS and the physical granules of this lane's two
-    // 16-byte pieces (logical granules h and 2 + h)
-    int aoff[4], boff[4], ga0[4], ga1[4], gb0[4], gb1[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int ra = wm * 128 + i * 32 + r32, rb = wn * 128 + i * 32 + r32;
-        aoff[i] = ra * TK;
-        boff[i] = rb * TK;
-        ga0[i] = ((0 + h) ^ swz(ra)) * 16;
-        ga1[i] = ((2 + h) ^ swz(ra)) * 16;
-        gb0[i] = ((0 + h) ^ swz(rb)) * 16;
-        gb1[i] = ((2 + h) ^ swz(rb)) * 16;
-    }
-    // scale offsets (chunk 0) of this lane for the units 2w, 2w + 1 it loads:
-    // lane l carries row 32 u + l % 32 and K-block half l / 32
-    uint32_t soff[2], toff[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int64_t ra = clamp64(T.a_row0 + (2 * w + u) * 32 + r32, 0, T.a_lim - 1);
-        const int64_t rb = clamp64(T.b_row0 + (2 * w + u) * 32 + r32, 0, T.b_lim - 1);
-        soff[u] = (uint32_t)((ra >> 5) * T.a_unit + 4 * (32 * h + (ra & 31)));
-        toff[u] = (uint32_t)((rb >> 5) * T.b_unit + 4 * (32 * h + (rb & 31)));
-    }
-
-    f32x16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-    const int64_t nchunk = (T.k1 - T.k0) / 256;
-    if (nchunk > 0) {
-        // Pipeline over stages j (K bytes [k0 + 64 j, k0 + 64 j + 64), LDS
-        // buffer j % 4; scales of chunk c in LDS buffer c % 2), with the
-        // fragments of the current step already in registers:
-        //   prologue: DMA scales(0), stages 0-3; wait for stage 0; read its
-        //     fragments and the chunk-0 scales.
-        //   step s: wait for stage s + 1; barrier (every wave is done reading
-        //     stage s's buffer); DMA stage s + 4 into it (step 4c also DMAs
-        //     scales(c + 1) first); read the fragments of stage s + 1 into
-        //     the other register set; 16 MFMAs on stage s.
-        // vmcnt bounds (operations issued after the stage waited for): 24 in
-        // the prologue; 16, 20, 20, 16 at steps 4c .. 4c + 3; in the last
-        // chunk (no scales, reload DMAs instead of new stages) 16, 16, 16 and
-        // no wait at step 4c + 3.
-        const uint8_t* As = T.As + (T.k0 / 256) * 256;
-        const uint8_t* Bs = T.Bs + (T.k0 / 256) * 256;
-        const uint8_t* ak = abase + T.k0;
-        const uint8_t* bk = bbase + T.k0;
-        uint32_t sa[4], sb[4], na[4], nb[4];
-        Frags F0, F1;
-        issue_scales(As, Bs, soff, toff, 0, w);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) issue_stage(ak + j * TK, bk + j * TK, aoffs, boffs, j, w);
-        wait_vm<3 * kDmaPerStage>();
-        __syncthreads();
-        read_frags(0, aoff, boff, ga0, ga1, gb0, gb1, F0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sa[i] = lds_sa[0][wm * 4 + i][l];
-            sb[i] = lds_sb[0][wn * 4 + i][l];
-        }
-        for (int64_t c = 0; c < nchunk; ++c) {
-            const bool last = c + 1 == nchunk;
-            const int par = (int)(c & 1);
-            const uint8_t* akc = ak + c * 256;
-            const uint8_t* bkc = bk + c * 256;
-            // stage fetched during step 4c + s: 4c + s + 4, or (last chunk) a
-            // reload of stage 4c + s into the buffer it already occupies
-            const int64_t ahead = last ? 0 : 4 * TK;
-            // step 4c: stage 4c in F0
-            wait_vm<2 * kDmaPerStage>();
-            __syncthreads();
-            read_frags(1, aoff, boff, ga0, ga1, gb0, gb1, F1);
-            if (!last) issue_scales(As + (c + 1) * 256, Bs + (c + 1) * 256, soff, toff, par ^ 1, w);
-            mfma_step<0>(F0, sa, sb, acc, akc + ahead, bkc + ahead, 0, aoffs, boffs, w);
-            pin_acc(acc);
-            // step 4c + 1: stage 4c + 1 in F1
-            if (!last) wait_vm<2 * kDmaPerStage + kScaleDma>();
-            else wait_vm<2 * kDmaPerStage>();
-            __syncthreads();
-            read_frags(2, aoff, boff, ga0, ga1, gb0, gb1, F0);
-            mfma_step<1>(F1, sa, sb, acc, akc + TK + ahead, bkc + TK + ahead, 1, aoffs, boffs, w);
-            pin_acc(acc);
-            // step 4c + 2: stage 4c + 2 in F0
-            if (!last) wait_vm<2 * kDmaPerStage + kScaleDma>();
-            else wait_vm<2 * kDmaPerStage>();
-            __syncthreads();
-            read_frags(3, aoff, boff, ga0, ga1, gb0, gb1, F1);
-            mfma_step<2>(F0, sa, sb, acc, akc + 2 * TK + ahead, bkc + 2 * TK + ahead, 2, aoffs, boffs, w);
-            pin_acc(acc);
-            // step 4c + 3: stage 4c + 3 in F1; fetch chunk c + 1's first
-            // fragments and scales
-            if (!last) {
-                wait_vm<2 * kDmaPerStage>();
-                __syncthreads();
-                read_frags(0, aoff, boff, ga0, ga1, gb0, gb1, F0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    na[i] = lds_sa[par ^ 1][wm * 4 + i][l];
-                    nb[i] = lds_sb[par ^ 1][wn * 4 + i][l];
-                }
-            }
-            mfma_step<3>(F1, sa, sb, acc, akc + 3 * TK + ahead, bkc + 3 * TK + ahead, 3, aoffs, boffs, w);
-            pin_acc(acc);
-            if (!last) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sa[i] = na[i];
-                    sb[i] = nb[i];
-                }
-            }
-        }
-    }
-    // Epilogue.  acc[i][j] is the 32 x 32 block (A rows 32 i.., B rows 32 j..)
-    // of this wave's 128 x 128 share, transposed by the operand order above:
-    // lane l holds output row 32 i + l % 32 and, in element 4 q + u, output
-    // column 32 j + 8 q + 4 (l / 32) + u -- four consecutive bf16 columns,
-    // stored as one 8-byte write when the row pitch allows it.  The lane bases
-    // are made opaque here so that the compiler does not hoist all the
-    // row/address values out of the persistent tile loop.
-    int rb = wm * 128 + r32;
-    int cb = wn * 128 + 4 * h;
-    uint32_t ldo = (uint32_t)T.ldo;
-    asm volatile("" : "+v"(rb), "+v"(cb), "+s"(ldo));
-    const bool vec = (ldo & 3) == 0 && (((uintptr_t)T.out) & 7) == 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = rb + i * 32;
-        if (row >= T.rows) continue;
-        uint16_t* const orow = T.out + (uint32_t)row * ldo;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
+        Fn.a[i] = lds_frag(la + i * 32 * SK, Ln.fo[0] ^ x, Ln.fo[1] ^ x);
+        Fn.b[i] = lds_frag(lb + i * 32 * SK, Ln.fo[2] ^ x, Ln.fo[3] ^ x);
+        if (DMA) {
+            const bool isb = i >= 2;
+            const i32x4& rs = isb ? S.rb : S.ra;
+            uint32_t& so = isb ? sob : soa;
+            uint32_t& lbr = isb ? lbb : lba;
+            const uint32_t ld8 = isb ? L.ldb * 8u : L.lda * 8u;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int col = cb + j * 32 + q * 8;
-                const __bf16 b0 = (__bf16)acc[i][j][4 * q + 0], b1 = (__bf16)acc[i][j][4 * q + 1];
-                const __bf16 b2 = (__bf16)acc[i][j][4 * q + 2], b3 = (__bf16)acc[i][j][4 * q + 3];
-                if (vec && col + 4 <= T.cols) {
-                    const uint2 pk = make_uint2(
-                        (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16),
-                        (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16));
-                    *reinterpret_cast<uint2*>(orow + col) = pk;
-                } else {
-                    if (col + 0 < T.cols) orow[col + 0] = __builtin_bit_cast(uint16_t, b0);
-                    if (col + 1 < T.cols) orow[col + 1] = __builtin_bit_cast(uint16_t, b1);
-                    if (col + 2 < T.cols) orow[col + 2] = __builtin_bit_cast(uint16_t, b2);
-                    if (col + 3 < T.cols) orow[col + 3] = __builtin_bit_cast(uint16_t, b3);
-                }
+                const uint32_t v = isb ? Ln.vb[q & 1] : Ln.va[q & 1];
+                if (i < 3)
+                    bdma16_run(rs, v, so, lbr, ld8, F.a[i], F.a[i + 1]);
+                else
+                    bdma16_run_after(rs, v, so, lbr, ld8, F.a[i]);
             }
+        } else if (i < 3) {
+            order_between(F.a[i], F.a[i + 1]);
+        }
     }
-    // the next tile reuses the LDS buffers
-    __syncthreads();
 }
 
-__device__ __forceinline__ void run_tile(const Tile& T) { run_tile_impl(T); }
+// Loads issued during a chunk: the scales of the following chunk and the two
+// following stages (of this tile, or of the next one in a tile's last chunk).
+struct Ahead {
+    i32x4 ra, rb, rsa, rsb;
+    int32_t asub, bsub;
+    uint32_t choff;         // contraction offset (bytes) of the scale chunk
+    uint32_t soff2, soff3;  // contraction offsets of the two stages
+};
+
+// Pipeline state carried from step to step.
+struct Pipe {
+    Frags F0, F1;          // fragments of the current / next step
+    uint32_t sa[4], sb[4];  // scale dwords of the current chunk
+    int gpar;              // scale parity of the current chunk
+};
+
+// One 256-wide contraction chunk = K steps 4c .. 4c + 3 = stages 2c (buffer
+// 0) and 2c + 1 (buffer 1).  Step s multiplies the fragments read during
+// step s - 1 and reads those of step s + 1:
+//   4c     F0 x, read F1 <- buffer 0 half 1
+//   4c + 1 wait for stage 2c + 1, barrier; F1 x, read F0 <- buffer 1 half 0;
+//          load the scales of the next chunk and stage 2c + 2 (buffer 0)
+//   4c + 2 F0 x, read F1 <- buffer 1 half 1
+//   4c + 3 wait for stage 2c + 2 and the scales, barrier; F1 x, read F0 <-
+//          buffer 0 half 0 and the next chunk's scales; load stage 2c + 3
+//          (buffer 1)
+// The barrier at 4c + 1 also frees buffer 0 (last read at step 4c), the one
+// at 4c + 3 buffer 1 (last read at 4c + 2).  vmcnt bounds: at 4c + 1 nothing
+// was issued after stage 2c + 1, except the 32 epilogue stores of the
+// previous tile (after_epilogue); at 4c + 3 nothing after stage 2c + 2.
+__device__ __forceinline__ void run_chunk(Pipe& P, f32x16 (&acc)[4][4], const Ahead& X, bool after_epilogue,
+                                          const Lane& Ln, const Layout& L, int w, int l, int wm, int wn,
+                                          uint32_t la0, uint32_t la1, uint32_t lb0, uint32_t lb1) {
+    const StageDma S2{X.ra, X.rb, X.soff2, la0, lb0};
+    const StageDma S3{X.ra, X.rb, X.soff3, la1, lb1};
+    // step 4c
+    mfma_step<0, false>(P.F0, P.F1, 0, 1, Ln, P.sa, P.sb, acc, S2, L);
+    pin_acc(acc);
+    // step 4c + 1
+    if (after_epilogue) wait_vm<32>();
+    else wait_vm<0>();
+    __syncthreads();
+    issue_scales(X.rsa, X.rsb, X.asub, X.bsub, X.choff, P.gpar ^ 1, w, l, L);
+    mfma_step<1, true>(P.F1, P.F0, 1, 0, Ln, P.sa, P.sb, acc, S2, L);
+    pin_acc(acc);
+    // step 4c + 2
+    mfma_step<2, false>(P.F0, P.F1, 1, 1, Ln, P.sa, P.sb, acc, S3, L);
+    pin_acc(acc);
+    // step 4c + 3
+    wait_vm<0>();
+    __syncthreads();
+    mfma_step<3, true>(P.F1, P.F0, 0, 0, Ln, P.sa, P.sb, acc, S3, L);
+    uint32_t na[4], nb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        na[i] = lds_sa[P.gpar ^ 1][wm * 4 + i][l];
+        nb[i] = lds_sb[P.gpar ^ 1][wn * 4 + i][l];
+    }
+    pin_acc(acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        P.sa[i] = na[i];
+        P.sb[i] = nb[i];
+    }
+    P.gpar ^= 1;
+}
 
 __device__ __forceinline__ int64_t group_lo(const int32_t* off, int g, int64_t M) {
     return clamp64(off[g], 0, M);
 }
 
+// Output tile of tile id `tile` (nchunk = 0 and empty descriptors when
+// tile >= total).  `g` is a search cursor: the tile ids a workgroup visits
+// increase, so the group of the next tile is found by walking forward from
+// the current one.
+__device__ __forceinline__ Tile decode_tile(const GemmArgs& a, const Layout& L, int64_t tile, int64_t total,
+                                            int& g) {
+    Tile T;
+    if (tile >= total) {
+        T.ra = T.rb = T.rsa = T.rsb = make_rsrc(a.A, 0);
+        T.asub = T.bsub = 0;
+        T.nchunk = 0;
+        T.rows = T.cols = 0;
+        T.out = a.out;
+        return T;
+    }
+    while (tile_end[g] <= tile) ++g;
+    g = (int)uni((uint32_t)g);
+    const int64_t first = g > 0 ? tile_end[g - 1] : 0;
+    const int64_t local = tile - first;
+    const uint8_t *B0, *Bs0;
+    int64_t arows, brows, k0, k1, arow0, brow0;
+    if (a.mode != 1) {
+        const int64_t nN = (a.N + TN - 1) / TN;
+        const int64_t o0 = group_lo(a.offsets, g, a.M);
+        const int64_t o1 = group_lo(a.offsets, g + 1, a.M);
+        const int64_t mg = o1 - o0;
+        const int64_t nM = (mg + TM - 1) / TM;
+        const int64_t band = local / (kBand * nN);
+        const int64_t gm = (nM - band * kBand) < kBand ? (nM - band * kBand) : kBand;
+        const int64_t r = local - band * kBand * nN;
+        const int64_t mt = band * kBand + r % gm;
+        const int64_t nt = r / gm;
+        arow0 = o0 + mt * TM;
+        arows = o1 - arow0;
+        k0 = 0;
+        k1 = a.K;
+        if (a.mode == 0) {
+            // expert g's weights: rows [g N, g N + N) of the [G N][K] matrix
+            brow0 = (int64_t)g * a.N + nt * TN;
+            brows = a.N - nt * TN;
+            B0 = a.B;
+            Bs0 = a.Bs;
+        } else {
+            // transposed weights [N][ldb]: expert g is the column slice
+            // [g K, g K + K), i.e. its contraction starts g K bytes (g K / 256
+            // scale chunks) into every row
+            brow0 = nt * TN;
+            brows = a.N - brow0;
+            B0 = a.B + (int64_t)g * a.K;
+            Bs0 = a.Bs + ((int64_t)g * a.K / 256) * 256;
+        }
+        T.out = a.out + arow0 * a.N + nt * TN;
+        T.rows = (int32_t)(arows < TM ? arows : TM);
+        T.cols = (int32_t)((a.N - nt * TN) < TN ? (a.N - nt * TN) : TN);
+    } else {
+        // wgrad: every non-empty group has the same tile grid over [N] x [K]
+        const int64_t nMt = (a.N + TM - 1) / TM;
+        const int64_t nNt = (a.K + TN - 1) / TN;
+        const int64_t band = local / (kBand * nNt);
+        const int64_t gm = (nMt - band * kBand) < kBand ? (nMt - band * kBand) : kBand;
+        const int64_t r = local - band * kBand * nNt;
+        const int64_t mt = band * kBand + r % gm;
+        const int64_t nt = r / gm;
+        k0 = clamp64(a.offsets[g], 0, a.Mcap) & ~(int64_t)255;
+        k1 = clamp64(a.offsets[g + 1], 0, a.Mcap) & ~(int64_t)255;
+        if (k1 < k0) k1 = k0;
+        arow0 = mt * TM;
+        arows = a.N - arow0;
+        brow0 = nt * TN;
+        brows = a.K - brow0;
+        B0 = a.B;
+        Bs0 = a.Bs;
+        T.out = a.out + (int64_t)g * a.N * a.K + arow0 * a.K + nt * TN;
+        T.rows = (int32_t)(arows < TM ? arows : TM);
+        T.cols = (int32_t)(brows < TN ? brows : TN);
+    }
+    const int64_t aso = (arow0 >> 5) * (int64_t)L.a_unit + (k0 / 256) * 256;
+    const int64_t bso = (Bs0 - a.Bs) + (brow0 >> 5) * (int64_t)L.b_unit + (k0 / 256) * 256;
+    const int64_t ar = arows < TM ? arows : TM, br = brows < TN ? brows : TN;
+    T.ra = make_rsrc(a.A + arow0 * (int64_t)L.lda + k0, (uint32_t)(ar * L.lda));
+    T.rb = make_rsrc(B0 + brow0 * (int64_t)L.ldb + k0, (uint32_t)(br * L.ldb));
+    T.rsa = make_rsrc(a.As + aso, (uint32_t)(a.a_scale_bytes - aso));
+    T.rsb = make_rsrc(a.Bs + bso, (uint32_t)(a.b_scale_bytes - bso));
+    T.asub = (int32_t)(arow0 & 31);
+    T.bsub = (int32_t)(brow0 & 31);
+    T.nchunk = (int32_t)((k1 - k0) / 256);
+    return T;
+}
+
+// Epilogue.  acc[i][j] is the 32 x 32 block (A rows 32 i.., B rows 32 j..)
+// of this wave's 128 x 128 share, transposed by the operand order of the
+// MFMAs: lane l holds output row 32 i + l % 32 and, in element 4 q + u,
+// output column 32 j + 8 q + 4 (l / 32) + u.  v_permlane32_swap gathers 8
+// consecutive columns per lane (lanes 0-31 columns 16 p + 0..7, lanes 32-63
+// 16 p + 8..15 for q = 2p, 2p + 1), stored with one 16-byte range-checked
+// store: rows past the tile's valid rows fall outside the descriptor and
+// columns past its valid columns get an offset outside it, so every wave
+// issues exactly 32 stores (the wait accounting of the next tile counts on
+// it).  Requires ldo % 8 == 0 (16-byte aligned rows).
+__device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y) << 16);
+}
+
+__device__ __forceinline__ void epilogue16(const Tile& T, const Layout& L, f32x16 (&acc)[4][4], int wm, int wn, int h,
+                                           int r32) {
+    const i32x4 ro = make_rsrc(T.out, (uint32_t)T.rows * L.ldo * 2u);
+    const uint32_t zero = uni(0u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t rowoff = (uint32_t)(wm * 128 + i * 32 + r32) * L.ldo * 2u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int q0 = 2 * p, q1 = 2 * p + 1;
+                const uint32_t x0 = pack_bf16x2(acc[i][j][4 * q0 + 0], acc[i][j][4 * q0 + 1]);
+                const uint32_t y0 = pack_bf16x2(acc[i][j][4 * q0 + 2], acc[i][j][4 * q0 + 3]);
+                const uint32_t x1 = pack_bf16x2(acc[i][j][4 * q1 + 0], acc[i][j][4 * q1 + 1]);
+                const uint32_t y1 = pack_bf16x2(acc[i][j][4 * q1 + 2], acc[i][j][4 * q1 + 3]);
+                const auto sx = __builtin_amdgcn_permlane32_swap(x0, x1, false, false);
+                const auto sy = __builtin_amdgcn_permlane32_swap(y0, y1, false, false);
+                const int col = wn * 128 + j * 32 + 16 * p + 8 * h;
+                const uint32_t off = col < T.cols ? rowoff + (uint32_t)col * 2u : 0xFFFFFFF0u;
+                bstore16(ro, off, zero, i32x4{(int)sx[0], (int)sy[0], (int)sx[1], (int)sy[1]});
+            }
+    }
+}
+
+// General epilogue for row strides that are not a multiple of 8 elements:
+// per-element stores with explicit bounds; drains its stores before
+// returning, so the wait accounting of the next tile needs no store count.
+__device__ __forceinline__ void epilogue_any(uint16_t* out, int rows, int cols, uint32_t ldo, f32x16 (&acc)[4][4],
+                                          int wm, int wn, int h, int r32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = wm * 128 + i * 32 + r32;
+        if (row >= rows) continue;
+        uint16_t* const orow = out + (uint32_t)row * ldo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int col = wn * 128 + j * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+                if (col < cols) orow[col] = __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][e]);
+            }
+    }
+    wait_vm<0>();
+}
+
+// VEC16: output rows are 16-byte aligned (ldo % 8 == 0): 16-byte epilogue.
+template <bool VEC16>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs a) {
     const int t = threadIdx.x;
+    const int w = t >> 6;
+    const int l = t & 63;
+    const int wm = w >> 1, wn = w & 1;
+    const int h = l >> 5, r32 = l & 31;
     const int nwg = gridDim.x;
     const int bid = blockIdx.x;
     // workgroup -> slot so that each XCD (bid % 8) owns a contiguous slot range
     const int slot = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
 
-    if (a.mode != 1) {
-        const int64_t nN = (a.N + TN - 1) / TN;
-        // per-group tile counts and their inclusive prefix (16 per thread)
-        const int G = a.G;
+    Layout L;
+    if (a.mode == 1) {
+        L.lda = (uint32_t)a.Mcap;
+        L.ldb = (uint32_t)a.Mcap;
+        L.a_unit = (uint32_t)a.Mcap;
+        L.b_unit = (uint32_t)a.Mcap;
+        L.ldo = (uint32_t)a.K;
+    } else {
+        L.lda = (uint32_t)a.K;
+        L.ldb = (uint32_t)(a.mode == 0 ? a.K : a.ldb);
+        L.a_unit = (uint32_t)a.K;
+        L.b_unit = (uint32_t)(a.mode == 0 ? a.K : a.ldb);
+        L.ldo = (uint32_t)a.N;
+    }
+
+    // Per-group tile counts and their inclusive prefix (16 groups per thread):
+    // modes 0/2 tile a group's rows; mode 1 gives every group with a
+    // non-empty contraction range the full [N] x [K] grid.
+    const int G = a.G;
+    const int64_t nN = (a.N + TN - 1) / TN;
+    const int64_t per1 = ((a.N + TM - 1) / TM) * ((a.K + TN - 1) / TN);
+    {
         int32_t loc[16];
         int32_t sum = 0;
 #pragma unroll
@@ -455,9 +569,15 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs a) {
             const int g = t * 16 + j;
             int32_t cnt = 0;
             if (g < G) {
-                const int64_t lo = group_lo(a.offsets, g, a.M), hi = group_lo(a.offsets, g + 1, a.M);
-                const int64_t mg = hi > lo ? hi - lo : 0;
-                cnt = (int32_t)(((mg + TM - 1) / TM) * nN);
+                if (a.mode != 1) {
+                    const int64_t lo = group_lo(a.offsets, g, a.M), hi = group_lo(a.offsets, g + 1, a.M);
+                    const int64_t mg = hi > lo ? hi - lo : 0;
+                    cnt = (int32_t)(((mg + TM - 1) / TM) * nN);
+                } else {
+                    const int64_t p0 = clamp64(a.offsets[g], 0, a.Mcap) & ~(int64_t)255;
+                    const int64_t p1 = clamp64(a.offsets[g + 1], 0, a.Mcap) & ~(int64_t)255;
+                    cnt = p1 > p0 ? (int32_t)per1 : 0;
+                }
             }
             sum += cnt;
             loc[j] = sum;
@@ -476,103 +596,107 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs a) {
         for (int j = 0; j < 16; ++j)
             if (t * 16 + j < G) tile_end[t * 16 + j] = base + loc[j];
         __syncthreads();
-        const int32_t total = G > 0 ? tile_end[G - 1] : 0;
-
-        for (int64_t tile = slot; tile < total; tile += nwg) {
-            // group: first g with tile_end[g] > tile
-            int lo = 0, hi = G - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (tile_end[mid] > tile) hi = mid;
-                else lo = mid + 1;
-            }
-            const int g = lo;
-            const int64_t first = g > 0 ? tile_end[g - 1] : 0;
-            const int64_t local = tile - first;
-            const int64_t o0 = group_lo(a.offsets, g, a.M);
-            const int64_t o1 = group_lo(a.offsets, g + 1, a.M);
-            const int64_t mg = o1 - o0;
-            const int64_t nM = (mg + TM - 1) / TM;
-            const int64_t band = local / (kBand * nN);
-            const int64_t gm = (nM - band * kBand) < kBand ? (nM - band * kBand) : kBand;
-            const int64_t r = local - band * kBand * nN;
-            const int64_t mt = band * kBand + r % gm;
-            const int64_t nt = r / gm;
-
-            Tile T;
-            T.A = a.A;
-            T.As = a.As;
-            T.lda = a.K;
-            T.a_unit = 32 * (a.K / 32);
-            T.a_row0 = o0 + mt * TM;
-            T.a_lim = o1;
-            if (a.mode == 0) {
-                // expert g's weights: rows [g N, g N + N) of the [G N][K] matrix
-                T.B = a.B;
-                T.Bs = a.Bs;
-                T.ldb = a.K;
-                T.b_unit = 32 * (a.K / 32);
-                T.b_row0 = (int64_t)g * a.N + nt * TN;
-                T.b_lim = (int64_t)g * a.N + a.N;
-            } else {
-                // transposed weights [N][ldb]: expert g is the column slice
-                // [g K, g K + K), i.e. its contraction starts g K bytes (g K / 256
-                // scale chunks) into every row
-                T.B = a.B + (int64_t)g * a.K;
-                T.Bs = a.Bs + ((int64_t)g * a.K / 256) * 256;
-                T.ldb = a.ldb;
-                T.b_unit = 32 * (a.ldb / 32);
-                T.b_row0 = nt * TN;
-                T.b_lim = a.N;
-            }
-            T.k0 = 0;
-            T.k1 = a.K;
-            T.out = a.out + (o0 + mt * TM) * a.N + nt * TN;
-            T.ldo = a.N;
-            T.rows = (int32_t)((mg - mt * TM) < TM ? (mg - mt * TM) : TM);
-            T.cols = (int32_t)((a.N - nt * TN) < TN ? (a.N - nt * TN) : TN);
-            run_tile(T);
-        }
-    } else {
-        // wgrad: every group has the same tile grid over [N] x [K]
-        const int64_t nMt = (a.N + TM - 1) / TM;
-        const int64_t nNt = (a.K + TN - 1) / TN;
-        const int64_t per = nMt * nNt;
-        const int64_t total = per * a.G;
-        for (int64_t tile = slot; tile < total; tile += nwg) {
-            const int64_t g = tile / per;
-            const int64_t local = tile - g * per;
-            const int64_t band = local / (kBand * nNt);
-            const int64_t gm = (nMt - band * kBand) < kBand ? (nMt - band * kBand) : kBand;
-            const int64_t r = local - band * kBand * nNt;
-            const int64_t mt = band * kBand + r % gm;
-            const int64_t nt = r / gm;
-            int64_t p0 = clamp64(a.offsets[g], 0, a.Mcap) & ~(int64_t)255;
-            int64_t p1 = clamp64(a.offsets[g + 1], 0, a.Mcap) & ~(int64_t)255;
-            if (p1 < p0) p1 = p0;
-
-            Tile T;
-            T.A = a.A;
-            T.As = a.As;
-            T.lda = a.Mcap;
-            T.a_unit = 32 * (a.Mcap / 32);
-            T.a_row0 = mt * TM;
-            T.a_lim = a.N;
-            T.B = a.B;
-            T.Bs = a.Bs;
-            T.ldb = a.Mcap;
-            T.b_unit = 32 * (a.Mcap / 32);
-            T.b_row0 = nt * TN;
-            T.b_lim = a.K;
-            T.k0 = p0;
-            T.k1 = p1;
-            T.out = a.out + g * a.N * a.K + mt * TM * a.K + nt * TN;
-            T.ldo = a.K;
-            T.rows = (int32_t)((a.N - mt * TM) < TM ? (a.N - mt * TM) : TM);
-            T.cols = (int32_t)((a.K - nt * TN) < TN ? (a.K - nt * TN) : TN);
-            run_tile(T);
-        }
     }
+    const int64_t total = G > 0 ? tile_end[G - 1] : 0;
+
+    if (a.mode == 1) {
+        // groups with an empty contraction range: dW[g] = 0
+        for (int64_t g = 0; g < G; ++g) {
+            const int64_t p0 = clamp64(a.offsets[g], 0, a.Mcap) & ~(int64_t)255;
+            const int64_t p1 = clamp64(a.offsets[g + 1], 0, a.Mcap) & ~(int64_t)255;
+            if (p1 > p0) continue;
+            uint16_t* const dst = a.out + g * a.N * a.K;
+            const int64_t n = a.N * a.K;
+            for (int64_t e = (int64_t)slot * 256 + t; e < n; e += (int64_t)nwg * 256) dst[e] = 0;
+        }
+        wait_vm<0>();
+    }
+
+    int64_t tile = slot;
+    if (tile >= total) return;
+
+    // per-lane constants
+    Lane Ln;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int row = w * 64 + (l >> 3);
+        const int gran = (l & 7) ^ (((l >> 4) & 3) | (p << 2));
+        Ln.va[p] = (uint32_t)row * L.lda + (uint32_t)gran * 16u;
+        Ln.vb[p] = (uint32_t)row * L.ldb + (uint32_t)gran * 16u;
+    }
+    {
+        const int ra = wm * 128 + r32, rb = wn * 128 + r32;
+        Ln.fo[0] = ra * SK + ((0 + h) ^ swz(ra)) * 16;
+        Ln.fo[1] = ra * SK + ((2 + h) ^ swz(ra)) * 16;
+        Ln.fo[2] = rb * SK + ((0 + h) ^ swz(rb)) * 16;
+        Ln.fo[3] = rb * SK + ((2 + h) ^ swz(rb)) * 16;
+    }
+    const uint32_t la0 = uni(lds_addr(lds_a[0]) + w * 64 * SK), la1 = uni(lds_addr(lds_a[1]) + w * 64 * SK);
+    const uint32_t lb0 = uni(lds_addr(lds_b[0]) + w * 64 * SK), lb1 = uni(lds_addr(lds_b[1]) + w * 64 * SK);
+
+    int gcur = 0;
+    Tile T = decode_tile(a, L, tile, total, gcur);
+
+    // Prologue: scales of chunk 0 into parity 0, stages 0 and 1 into buffers
+    // 0 and 1; wait for the scales and stage 0.
+    issue_scales(T.rsa, T.rsb, T.asub, T.bsub, uni(0u), 0, w, l, L);
+    {
+        const StageDma S0{T.ra, T.rb, uni(0u), la0, lb0};
+        const StageDma S1{T.ra, T.rb, uni((uint32_t)SK), la1, lb1};
+        issue_stage_plain(S0, Ln, L);
+        issue_stage_plain(S1, Ln, L);
+    }
+    wait_vm<kStageDma>();
+    __syncthreads();
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    Pipe P;
+    read_frags(0, 0, Ln, P.F0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        P.sa[i] = lds_sa[0][wm * 4 + i][l];
+        P.sb[i] = lds_sb[0][wn * 4 + i][l];
+    }
+    P.gpar = 0;
+    bool first = true;  // no epilogue stores issued yet
+
+    // The chunks of all of this workgroup's tiles form one pipeline: the last
+    // chunk of a tile loads the next tile's chunk-0 scales and stages 0 and 1
+    // (nothing, through empty descriptors, after the last tile).
+    for (;;) {
+        int c = 0;
+        for (; c + 1 < T.nchunk; ++c) {
+            const Ahead X{T.ra, T.rb, T.rsa, T.rsb, T.asub, T.bsub, uni((uint32_t)(c + 1) * 256u),
+                          uni((uint32_t)(2 * c + 2) * SK), uni((uint32_t)(2 * c + 3) * SK)};
+            run_chunk(P, acc, X, c == 0 && !first && VEC16, Ln, L, w, l, wm, wn, la0, la1, lb0, lb1);
+        }
+        const Tile Tn = decode_tile(a, L, tile + nwg, total, gcur);
+        {
+            const Ahead X{Tn.ra, Tn.rb, Tn.rsa, Tn.rsb, Tn.asub, Tn.bsub, uni(0u), uni(0u), uni((uint32_t)SK)};
+            run_chunk(P, acc, X, c == 0 && !first && VEC16, Ln, L, w, l, wm, wn, la0, la1, lb0, lb1);
+        }
+        if (VEC16) epilogue16(T, L, acc, wm, wn, h, r32);
+        else epilogue_any(T.out, T.rows, T.cols, L.ldo, acc, wm, wn, h, r32);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+        if (Tn.nchunk == 0) break;
+        T = Tn;
+        tile += nwg;
+        first = false;
+    }
+    // Loads through empty descriptors and the last stores: let them finish
+    // before the wave ends and its LDS is handed to another workgroup.
+    wait_vm<0>();
 }
 
 int num_cus() {
@@ -586,6 +710,16 @@ int num_cus() {
     }
     return cached[dev];
 }
+
+void launch(const GemmArgs& a, int64_t nwg, hipStream_t stream) {
+    const int64_t ldo = a.mode == 1 ? a.K : a.N;
+    if (ldo % 8 == 0)
+        hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3((unsigned)nwg), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3((unsigned)nwg), dim3(256), 0, stream, a);
+}
+
+int64_t scale_bytes(int64_t R, int64_t K) { return ((R + 31) / 32) * 32 * (8 * ((K + 255) / 256)); }
 
 }  // namespace
 
@@ -604,13 +738,15 @@ hipError_t launch_grouped_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8
     a.N = N;
     a.K = K;
     a.Mcap = 0;
+    a.a_scale_bytes = scale_bytes(M, K);
+    a.b_scale_bytes = scale_bytes((int64_t)G * N, K);
     a.G = G;
     a.mode = 0;
     a.ldb = 0;
     const int64_t ub = ((M + TM - 1) / TM + G) * ((N + TN - 1) / TN);
     int64_t nwg = num_cus();
     if (ub < nwg) nwg = ub;
-    hipLaunchKernelGGL(grouped_gemm_kernel, dim3((unsigned)nwg), dim3(256), 0, stream, a);
+    launch(a, nwg, stream);
     return hipGetLastError();
 }
 
@@ -629,13 +765,15 @@ hipError_t launch_grouped_gemm_dgrad(const uint8_t* dYq, const uint8_t* dYs, con
     a.N = N;
     a.K = K;
     a.Mcap = 0;
+    a.a_scale_bytes = scale_bytes(M, K);
+    a.b_scale_bytes = scale_bytes(N, Wcap);
     a.G = G;
     a.mode = 2;
     a.ldb = Wcap;
     const int64_t ub = ((M + TM - 1) / TM + G) * ((N + TN - 1) / TN);
     int64_t nwg = num_cus();
     if (ub < nwg) nwg = ub;
-    hipLaunchKernelGGL(grouped_gemm_kernel, dim3((unsigned)nwg), dim3(256), 0, stream, a);
+    launch(a, nwg, stream);
     return hipGetLastError();
 }
 
@@ -655,13 +793,15 @@ hipError_t launch_grouped_gemm_wgrad(const uint8_t* A, const uint8_t* As, const 
     a.N = N;
     a.K = K;
     a.Mcap = Mcap;
+    a.a_scale_bytes = scale_bytes(N, Mcap);
+    a.b_scale_bytes = scale_bytes(K, Mcap);
     a.G = G;
     a.mode = 1;
     a.ldb = 0;
     const int64_t total = ((N + TM - 1) / TM) * ((K + TN - 1) / TN) * G;
     int64_t nwg = num_cus();
     if (total < nwg) nwg = total;
-    hipLaunchKernelGGL(grouped_gemm_kernel, dim3((unsigned)nwg), dim3(256), 0, stream, a);
+    launch(a, nwg, stream);
     return hipGetLastError();
 }
 
