@@ -11,6 +11,10 @@ Throughput = algorithmic bytes (2 B read + 1 B + 1/32 B written per element,
 per pass; the byte count of the lpnh.cn 2479732 section 4 benchmark with bf16
 input) / GPU time, inputs resident in HBM.
 
+``quantize_dual`` times the dual-layout quantize on the same input (one read,
+row-wise and column-wise results: 2 B read + 2 x (1 + 1/32) B written per
+element) next to the two separate passes.
+
 The ``gemm`` object times the grouped GEMMs on the MoE workloads (TFLOP/s =
 2 M N K over real rows / GPU time): gate+up (32768 x 7168 -> 4096, 16 experts),
 the ragged 128-expert case next to the dense GEMM of the same size, and the
@@ -137,21 +141,30 @@ def bench_quant(torch, mx, W, args):
     def cols():
         mx.mx_quantize_cols(x, None, Mcap, qT, sT)
 
+    def dual():
+        mx.mx_quantize_dual(x, None, Mcap, q, s, qT, sT)
+
     for _ in range(args.warmup):
         rows()
         cols()
+        dual()
     torch.cuda.synchronize()
     tm = Timer(torch)
     t0 = time.perf_counter()
     ms_rows = tm.run(rows, args.steps)
     ms_cols = tm.run(cols, args.steps)
+    ms_dual = tm.run(dual, args.steps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     nbytes = quant_bytes(M, K)
+    dual_bytes = 2 * M * K + 2 * (M * K + M * K // 32)  # one read, both results written
     res = {
         "M": M, "K": K, "ms_rows": ms_rows, "ms_cols": ms_cols, "wall_s": wall,
         "bytes_per_pass": nbytes,
         "tbs_rows": nbytes / ms_rows / 1e9, "tbs_cols": nbytes / ms_cols / 1e9,
+        "dual": {"ms": ms_dual, "bytes": dual_bytes, "tbs": dual_bytes / ms_dual / 1e9,
+                 "frac_hbm_peak": dual_bytes / ms_dual / 1e9 / HBM_PEAK_TBS,
+                 "ms_rows_plus_cols": ms_rows + ms_cols, "speedup_vs_two_passes": (ms_rows + ms_cols) / ms_dual},
     }
     sample = None
     if not args.no_cpu:
@@ -308,6 +321,7 @@ def main():
                      "unit": "GB/s", "frac": achieved / (HBM_PEAK_TBS * 1000), "traffic": traffic,
                      "algorithmic_bytes_per_launch": quant["bytes_per_pass"]},
         "cpu_baseline": cpu,
+        "quantize_dual": dict(quant["dual"], workload="bf16 [131072, 7168] -> row-wise + column-wise MXFP8, one read"),
         "gemm": gemm,
     }
     print(json.dumps(line), flush=True)

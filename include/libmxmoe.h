@@ -113,6 +113,27 @@ mx_status mx_quantize_cols(const uint16_t* x, int64_t M, int64_t N, int64_t ldx,
                            int64_t Mcap, int32_t* padded_offsets, void* stream);
 
 /*
+ * Dual-layout quantization: one read of x, both results.  The backward pass
+ * needs a bf16 gradient quantized along both of its axes (lpnh.cn 2479732
+ * section 1: the backward pass adds a transposed quantization; aigc.bar
+ * "被忽视的量化税": the quantization passes are pure memory traffic), so
+ * reading it once moves 4.06 instead of 6.06 bytes per element.
+ *   q, s    exactly the outputs of mx_quantize_rows(x, M, N, ldx, q, s)
+ *           (codes uint8 [M][N], packed scales R = M, contraction N)
+ *   qT, sT, padded_offsets  exactly the outputs of
+ *           mx_quantize_cols(x, M, N, ldx, group_offsets, G, qT, sT, Mcap,
+ *           padded_offsets)
+ * provided the group offsets follow the convention above (first 0, last M):
+ * the row-wise result covers the rows that lie in a group.  Requires
+ * N % 32 == 0 (MX_ERR_SHAPE otherwise) and the alignment and capacity rules
+ * of both calls; all buffers are caller-owned device memory.
+ */
+mx_status mx_quantize_dual(const uint16_t* x, int64_t M, int64_t N, int64_t ldx,
+                           const int32_t* group_offsets, int32_t G, uint8_t* q, uint8_t* s,
+                           uint8_t* qT, uint8_t* sT, int64_t Mcap, int32_t* padded_offsets,
+                           void* stream);
+
+/*
  * Grouped GEMM (M-grouped; forward and dgrad): rows [o_g, o_{g+1}) of X use
  * expert g's weights (aigc.bar "为MoE量身定制优化"; lpnh.cn 2479732 section 1):
  *   out[m][n] = sum_k deq(Xq[m][k]) * deq(Wq[g][n][k]),   fp32 accumulation,

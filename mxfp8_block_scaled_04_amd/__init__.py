@@ -45,6 +45,8 @@ def load():
     lib.mx_quantize_rows.restype = ST
     lib.mx_quantize_cols.argtypes = [P, I64, I64, I64, P, I32, P, P, I64, P, P]
     lib.mx_quantize_cols.restype = ST
+    lib.mx_quantize_dual.argtypes = [P, I64, I64, I64, P, I32, P, P, P, P, I64, P, P]
+    lib.mx_quantize_dual.restype = ST
     lib.mx_grouped_gemm.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, P]
     lib.mx_grouped_gemm.restype = ST
     lib.mx_grouped_gemm_dgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, I64, P, P]
@@ -58,7 +60,7 @@ def load():
 # Exported C symbols, in header order.
 SYMBOLS = (
     "mx_status_str", "mx_version", "mx_scale_bytes", "mx_cols_capacity", "mx_quantize_rows",
-    "mx_quantize_cols", "mx_grouped_gemm", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad",
+    "mx_quantize_cols", "mx_quantize_dual", "mx_grouped_gemm", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad",
 )
 
 
@@ -130,6 +132,32 @@ def mx_quantize_cols(x, group_offsets=None, Mcap=None, qT=None, sT=None, padded_
                                  _ptr(padded_offsets), _stream(stream))
     _check(rc, "mx_quantize_cols")
     return qT, sT, padded_offsets
+
+
+def mx_quantize_dual(x, group_offsets=None, Mcap=None, q=None, s=None, qT=None, sT=None, padded_offsets=None,
+                     stream=None):
+    """Row-wise and column-wise MXFP8 of bf16 x [M, N] from one read.
+    Returns (q, s, qT, sT, padded_offsets): the results of mx_quantize_rows and
+    mx_quantize_cols."""
+    x = _bits16(x)
+    M, N = x.shape
+    G = 1 if group_offsets is None else group_offsets.numel() - 1
+    if Mcap is None:
+        Mcap = mx_cols_capacity(M, G)
+    if q is None:
+        q = torch.empty((M, N), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty(mx_scale_bytes(M, N), dtype=torch.uint8, device=x.device)
+    if qT is None:
+        qT = torch.empty((N, Mcap), dtype=torch.uint8, device=x.device)
+    if sT is None:
+        sT = torch.empty(mx_scale_bytes(N, Mcap), dtype=torch.uint8, device=x.device)
+    if group_offsets is not None and padded_offsets is None:
+        padded_offsets = torch.empty(G + 1, dtype=torch.int32, device=x.device)
+    rc = load().mx_quantize_dual(_ptr(x), M, N, x.stride(0), _ptr(group_offsets), G, _ptr(q), _ptr(s), _ptr(qT),
+                                 _ptr(sT), Mcap, _ptr(padded_offsets), _stream(stream))
+    _check(rc, "mx_quantize_dual")
+    return q, s, qT, sT, padded_offsets
 
 
 def mx_grouped_gemm(Xq, Xs, Wq, Ws, group_offsets, out=None, stream=None):

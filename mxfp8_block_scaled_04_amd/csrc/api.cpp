@@ -75,6 +75,28 @@ mx_status mx_quantize_cols(const uint16_t* x, int64_t M, int64_t N, int64_t ldx,
                                              (hipStream_t)stream));
 }
 
+mx_status mx_quantize_dual(const uint16_t* x, int64_t M, int64_t N, int64_t ldx, const int32_t* group_offsets,
+                           int32_t G, uint8_t* q, uint8_t* s, uint8_t* qT, uint8_t* sT, int64_t Mcap,
+                           int32_t* padded_offsets, void* stream) {
+    if (group_offsets == nullptr) G = 1;
+    if (M < 0 || N < 0 || N % 32 != 0 || ldx < N || Mcap < 0) return MX_ERR_SHAPE;
+    if (G < 1 || G > kMaxGroups) return MX_ERR_SHAPE;
+    if (Mcap % 256 != 0 || Mcap < mx_cols_capacity(M, G)) return MX_ERR_CAPACITY;
+    if (group_offsets != nullptr && padded_offsets == nullptr) return MX_ERR_NULL;
+    if (N == 0 || Mcap == 0) {
+        if (group_offsets == nullptr) return MX_OK;
+    } else {
+        if (!x && M > 0) return MX_ERR_NULL;
+        if (!qT || !sT || (M > 0 && (!q || !s))) return MX_ERR_NULL;
+        if ((x && !aligned16(x)) || !aligned16(qT) || !aligned16(sT) || (q && !aligned16(q)) ||
+            (s && !aligned16(s)) || ldx % 8 != 0)
+            return MX_ERR_ALIGN;
+    }
+    if (Mcap / 256 > 65535 || (N + 255) / 256 > (int64_t)UINT32_MAX / 256) return MX_ERR_UNSUPPORTED;  // grid
+    return from_hip(mx::launch_quantize_dual(x, M, N, ldx, group_offsets, G, q, s, qT, sT, Mcap, padded_offsets,
+                                             (hipStream_t)stream));
+}
+
 mx_status mx_grouped_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
                           const int32_t* group_offsets, int32_t G, int64_t M, int64_t N, int64_t K, uint16_t* out,
                           void* stream) {

@@ -13,6 +13,10 @@ hipError_t launch_quantize_cols(const uint16_t* x, int64_t M, int64_t N, int64_t
                                 const int32_t* group_offsets, int32_t G, uint8_t* qT, uint8_t* sT,
                                 int64_t Mcap, int32_t* padded_offsets, hipStream_t stream);
 
+hipError_t launch_quantize_dual(const uint16_t* x, int64_t M, int64_t N, int64_t ldx,
+                                const int32_t* group_offsets, int32_t G, uint8_t* q, uint8_t* s, uint8_t* qT,
+                                uint8_t* sT, int64_t Mcap, int32_t* padded_offsets, hipStream_t stream);
+
 hipError_t launch_grouped_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq,
                                const uint8_t* Ws, const int32_t* group_offsets, int32_t G, int64_t M,
                                int64_t N, int64_t K, uint16_t* out, hipStream_t stream);

@@ -71,6 +71,25 @@ def test_quantize_cols_validation():
     assert f(FAKE, 300, 64, 32, FAKE, 3, FAKE, FAKE, cap, FAKE, None) == 2        # ldx < N
 
 
+def test_quantize_dual_validation():
+    f = mx.load().mx_quantize_dual
+    cap = mx.mx_cols_capacity(300, 3)
+    ok = (FAKE, 300, 64, 64, FAKE, 3, FAKE, FAKE, FAKE, FAKE, cap, FAKE, None)
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a10=cap - 256) == 4                # capacity too small
+    assert call(a2=48, a3=64) == 2                 # N % 32 != 0
+    assert call(a3=32) == 2                        # ldx < N
+    assert call(a5=0) == 2                         # G < 1
+    assert call(a11=None) == 1                     # padded offsets required with groups
+    assert call(a6=None) == 1                      # NULL row-wise codes
+    assert call(a8=None) == 1                      # NULL column-wise codes
+    assert call(a6=P(0x100004)) == 3               # misaligned row-wise codes
+
+
 def test_grouped_gemm_validation():
     f = mx.load().mx_grouped_gemm
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 128, 288, FAKE, None) == 5  # K % 256 != 0
