@@ -21,6 +21,15 @@ Parity status of each function (what pins it in ``tests/test_oracle.py``):
   grouped_gemm(_points)              exact rational brute force on small shapes,
                                      one-hot closed form
   wgrad(_points)                     exact rational brute force on small shapes
+  silu                               closed forms (0, ln 3, large |x|), odd-part
+                                     identity silu(x) - silu(-x) = x
+  block_scale_f64 / quantize_f64_*   closed-form scale sweep; equal to the bf16
+                                     path on bf16 values; independent
+                                     table-search encoder on off-grid values
+  swiglu_quantize                    saturated-gate reduction to quantize_rows,
+                                     zero gate, quantization-error invariants
+  grouped_gemm_swiglu(_blocks)       one-hot routing closed form (expert and
+                                     gate/up roles), full vs sampled agreement
 """
 import ctypes
 import os
@@ -80,6 +89,13 @@ def _load():
     lib.mxref_grouped_gemm_points.argtypes = [P, P, P, P, P, ctypes.c_int32, I64, I64, I64, P, P, I64, P]
     lib.mxref_wgrad.argtypes = [P, P, P, P, P, ctypes.c_int32, I64, I64, I64, P]
     lib.mxref_wgrad_points.argtypes = [P, P, P, P, P, ctypes.c_int32, I64, I64, I64, P, P, P, I64, P]
+    lib.mxref_silu.argtypes = [ctypes.c_double]
+    lib.mxref_silu.restype = ctypes.c_double
+    lib.mxref_block_scale_f64.argtypes = [P, I64]
+    lib.mxref_block_scale_f64.restype = ctypes.c_uint8
+    lib.mxref_quantize_f64_with_scale.argtypes = [P, I64, ctypes.c_uint8, P]
+    lib.mxref_quantize_rows_f64.argtypes = [P, I64, I64, P, P]
+    lib.mxref_swiglu_quantize.argtypes = [P, P, I64, I64, P, P, P]
     _lib = lib
     return lib
 
@@ -232,3 +248,71 @@ def wgrad_points(Aq, As, Bq, Bs, padded, gs, ns, ks):
     _load().mxref_wgrad_points(pa, pas, pb, pbs, pp, P.size - 1, N, K, Mcap, pg, pn, pk, g.size,
                                out.ctypes.data_as(ctypes.c_void_p))
     return out
+
+
+# ---- SwiGLU + MXFP8 of its result (mxref.c states the readings) ----
+
+def silu(x):
+    return _load().mxref_silu(float(x))
+
+
+def block_scale_f64(x):
+    a, p = _c(x, np.float64)
+    return int(_load().mxref_block_scale_f64(p, a.size))
+
+
+def quantize_f64_with_scale(x, S):
+    a, p = _c(x, np.float64)
+    q = np.empty(a.size, np.uint8)
+    _load().mxref_quantize_f64_with_scale(p, a.size, int(S), q.ctypes.data_as(ctypes.c_void_p))
+    return q.reshape(np.shape(x))
+
+
+def quantize_rows_f64(x):
+    """double [M, K] -> (codes uint8 [M, K], canonical scales uint8 [M, K/32])."""
+    a, p = _c(x, np.float64)
+    M, K = a.shape
+    assert K % 32 == 0
+    q = np.empty((M, K), np.uint8)
+    s = np.empty((M, K // 32), np.uint8)
+    _load().mxref_quantize_rows_f64(p, M, K, q.ctypes.data_as(ctypes.c_void_p), s.ctypes.data_as(ctypes.c_void_p))
+    return q, s
+
+
+def swiglu_quantize(gate, up):
+    """gate, up double [M, I] -> (h = silu(gate) up [M, I], codes [M, I], scales [M, I/32])."""
+    g, pg = _c(gate, np.float64)
+    u, pu = _c(up, np.float64)
+    assert g.shape == u.shape and g.ndim == 2 and g.shape[1] % 32 == 0
+    M, I = g.shape
+    h = np.empty((M, I), np.float64)
+    q = np.empty((M, I), np.uint8)
+    s = np.empty((M, I // 32), np.uint8)
+    _load().mxref_swiglu_quantize(pg, pu, M, I, h.ctypes.data_as(ctypes.c_void_p), q.ctypes.data_as(ctypes.c_void_p),
+                                  s.ctypes.data_as(ctypes.c_void_p))
+    return h, q, s
+
+
+def grouped_gemm_swiglu(Xq, Xs, Wgq, Wgs, Wuq, Wus, offsets):
+    """MoE first projection and activation: gate = X Wg^T and up = X Wu^T per
+    expert (grouped_gemm), then swiglu_quantize.  Wgq, Wuq [G, I, K] codes,
+    Wgs, Wus [G, I, K/32] canonical scales.  Returns (h, codes, scales, gate, up);
+    rows outside every group have gate = up = 0."""
+    gate = grouped_gemm(Xq, Xs, Wgq, Wgs, offsets)
+    up = grouped_gemm(Xq, Xs, Wuq, Wus, offsets)
+    h, q, s = swiglu_quantize(gate, up)
+    return h, q, s, gate, up
+
+
+def grouped_gemm_swiglu_blocks(Xq, Xs, Wgq, Wgs, Wuq, Wus, offsets, rows, blocks):
+    """The same at sampled 32-wide blocks: for each (rows[i], blocks[i]) the
+    hidden units [32 b, 32 b + 32) of that row.  Returns (h, codes, gate, up)
+    as [n, 32] and scales [n]."""
+    rows = np.asarray(rows, np.int64)
+    blocks = np.asarray(blocks, np.int64)
+    r = np.repeat(rows, 32)
+    c = (blocks[:, None] * 32 + np.arange(32)[None, :]).reshape(-1)
+    gate = grouped_gemm_points(Xq, Xs, Wgq, Wgs, offsets, r, c).reshape(-1, 32)
+    up = grouped_gemm_points(Xq, Xs, Wuq, Wus, offsets, r, c).reshape(-1, 32)
+    h, q, s = swiglu_quantize(gate, up)
+    return h, q, s[:, 0], gate, up

@@ -80,12 +80,8 @@ uint8_t mxref_e4m3_encode(double y) {
     return (uint8_t)(code | (neg << 7));
 }
 
-uint8_t mxref_block_scale(const uint16_t* x, int64_t n, int64_t stride) {
-    double amax = 0.0;
-    for (int64_t i = 0; i < n; ++i) {
-        double a = fabs(mxref_bf16_value(x[i * stride]));
-        if (a > amax) amax = a;
-    }
+/* E8M0 scale byte of a block whose largest magnitude is amax. */
+static uint8_t scale_of_amax(double amax) {
     if (amax == 0.0) return 0;               /* floor(log2 0) = -inf, clamped to -127 */
     int e;
     (void)frexp(amax, &e);
@@ -93,6 +89,15 @@ uint8_t mxref_block_scale(const uint16_t* x, int64_t n, int64_t stride) {
     if (shared < -127) shared = -127;
     if (shared > 127) shared = 127;
     return (uint8_t)(shared + 127);
+}
+
+uint8_t mxref_block_scale(const uint16_t* x, int64_t n, int64_t stride) {
+    double amax = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double a = fabs(mxref_bf16_value(x[i * stride]));
+        if (a > amax) amax = a;
+    }
+    return scale_of_amax(amax);
 }
 
 void mxref_quantize_with_scale(const uint16_t* x, int64_t n, uint8_t S, uint8_t* q) {
@@ -273,4 +278,49 @@ void mxref_wgrad_points(const uint8_t* Aq, const uint8_t* As, const uint8_t* Bq,
     (void)N;
     (void)K;
     for (int64_t i = 0; i < npts; ++i) out[i] = wgrad_point(Aq, As, Bq, Bs, P, (int32_t)gs[i], ns[i], ks[i], Mcap);
+}
+
+/* ---- SwiGLU of the gate and up projections, quantized to MXFP8 ----
+ * The pages fuse the MXFP8 quantization of the activation into the SwiGLU
+ * step of the MoE layer (kucoin.com MoK page; aigc.bar "被忽视的量化税" on
+ * the cost of a separate quantization pass).  They give no formula.  Readings
+ * taken here:
+ *   - SwiGLU(gate, up) = silu(gate) * up with silu(x) = x * sigmoid(x) =
+ *     x / (1 + e^-x), elementwise (the usual gated-MLP activation);
+ *   - the result h is a real number (double here), quantized directly: one
+ *     scale per 32 consecutive hidden units of a row by the rule above,
+ *     applied to |h| itself, then y = h * 2^(127-S) encoded as E4M3FN with
+ *     saturation and nearest-even.  There is no intermediate bf16 rounding
+ *     of h.
+ */
+double mxref_silu(double x) {
+    return x / (1.0 + exp(-x));              /* exp(-x) = inf for x < -709: -0 */
+}
+
+uint8_t mxref_block_scale_f64(const double* x, int64_t n) {
+    double amax = 0.0;
+    for (int64_t i = 0; i < n; ++i)
+        if (fabs(x[i]) > amax) amax = fabs(x[i]);
+    return scale_of_amax(amax);
+}
+
+void mxref_quantize_f64_with_scale(const double* x, int64_t n, uint8_t S, uint8_t* q) {
+    for (int64_t i = 0; i < n; ++i) q[i] = mxref_e4m3_encode(ldexp(x[i], 127 - (int)S));
+}
+
+void mxref_quantize_rows_f64(const double* x, int64_t M, int64_t K, uint8_t* q, uint8_t* s) {
+    int64_t nb = K / 32;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t b = 0; b < nb; ++b) {
+            const double* blk = x + m * K + b * 32;
+            uint8_t S = mxref_block_scale_f64(blk, 32);
+            s[m * nb + b] = S;
+            mxref_quantize_f64_with_scale(blk, 32, S, q + m * K + b * 32);
+        }
+}
+
+void mxref_swiglu_quantize(const double* gate, const double* up, int64_t M, int64_t I, double* h, uint8_t* q,
+                           uint8_t* s) {
+    for (int64_t i = 0; i < M * I; ++i) h[i] = mxref_silu(gate[i]) * up[i];
+    mxref_quantize_rows_f64(h, M, I, q, s);
 }

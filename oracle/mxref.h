@@ -97,6 +97,16 @@ void mxref_wgrad_points(const uint8_t* Aq, const uint8_t* As, const uint8_t* Bq,
                         const int64_t* gs, const int64_t* ns, const int64_t* ks, int64_t npts,
                         double* out);
 
+/* SwiGLU + MXFP8 of its result (readings in mxref.c). */
+double mxref_silu(double x);
+uint8_t mxref_block_scale_f64(const double* x, int64_t n);
+void mxref_quantize_f64_with_scale(const double* x, int64_t n, uint8_t S, uint8_t* q);
+/* x double [M][K] (K % 32 == 0) -> codes [M][K], canonical scales [M][K/32] */
+void mxref_quantize_rows_f64(const double* x, int64_t M, int64_t K, uint8_t* q, uint8_t* s);
+/* gate, up double [M][I] -> h = silu(gate) up [M][I], its codes and scales */
+void mxref_swiglu_quantize(const double* gate, const double* up, int64_t M, int64_t I, double* h, uint8_t* q,
+                           uint8_t* s);
+
 #ifdef __cplusplus
 }
 #endif

@@ -448,3 +448,183 @@ def test_wgrad_matches_rowwise_gemm_of_padded_slices():
         bq, bs = oracle.quantize_rows(np.ascontiguousarray(b.T))
         ref = oracle.grouped_gemm(aq, as_, bq.reshape(1, K, span), bs.reshape(1, K, span // 32), np.array([0, N], np.int32))
         assert np.array_equal(ref, dW[g])
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU of the gate and up projections, quantized to MXFP8 (the activation
+# step of the MoE layer that the kucoin.com MoK page fuses with the
+# quantization): closed forms of silu, a closed-form scale sweep on real
+# values, the table-search encoder on off-grid values, and reductions to the
+# pinned bf16 quantizer.
+# ---------------------------------------------------------------------------
+
+
+def _ulps(a, b):
+    return abs(a - b) / math.ulp(max(abs(a), abs(b)))
+
+
+def test_silu_closed_forms():
+    ln3 = math.log(3.0)
+    assert oracle.silu(0.0) == 0.0
+    # sigmoid(ln 3) = 1 / (1 + 1/3) = 3/4, sigmoid(-ln 3) = 1/4
+    assert _ulps(oracle.silu(ln3), 0.75 * ln3) <= 4
+    assert _ulps(oracle.silu(-ln3), -0.25 * ln3) <= 4
+    # e^-64 is far below half an ulp of 1: silu(64) is 64 itself
+    assert oracle.silu(64.0) == 64.0
+    assert -64.0 * 2.0 ** -92 <= oracle.silu(-64.0) < 0.0
+    assert oracle.silu(-1000.0) == 0.0
+
+
+def test_silu_odd_part_identity():
+    """silu(x) - silu(-x) = x sigmoid(x) + x sigmoid(-x) = x."""
+    rng = np.random.default_rng(20)
+    for x in rng.uniform(-30.0, 30.0, 200):
+        d = oracle.silu(x) - oracle.silu(-x)
+        assert abs(d - x) <= 4 * math.ulp(abs(x)) + 1e-300
+
+
+def test_block_scale_f64_closed_form_sweep():
+    """amax = f 2^e with f in [1, 2): S = clamp(e - 8, -127, 127) + 127, for any
+    other elements below amax in magnitude and either sign of amax."""
+    rng = np.random.default_rng(21)
+    for e in range(-140, 140):
+        for f in (1.0, 1.0 + 2.0 ** -40, 1.5, 2.0 - 2.0 ** -45):
+            amax = math.ldexp(f, e)
+            blk = rng.uniform(-1.0, 1.0, 32) * amax * 0.999
+            blk[rng.integers(0, 32)] = amax if rng.integers(0, 2) else -amax
+            want = min(max(e - 8, -127), 127) + 127
+            assert oracle.block_scale_f64(blk) == want, (e, f)
+    assert oracle.block_scale_f64(np.zeros(32)) == 0
+    assert oracle.block_scale_f64(-np.zeros(32)) == 0
+
+
+def test_quantize_f64_matches_table_search_off_grid():
+    """Values between the E4M3 grid points, the exact midpoints (ties to even)
+    and their neighbours, beyond saturation and in the subnormal range."""
+    rng = np.random.default_rng(22)
+    pos = POS[np.isfinite(POS)]
+    mids = (pos[:-1] + pos[1:]) / 2
+    y = np.concatenate([
+        rng.uniform(-500.0, 500.0, 4000),
+        rng.uniform(-2.0 ** -6, 2.0 ** -6, 1000),
+        mids, -mids, np.nextafter(mids, 0), np.nextafter(mids, 1000),
+        [448.0, 463.99, 464.0, 1e30, -1e30, 2.0 ** -10, 2.0 ** -10 + 2.0 ** -60, 3 * 2.0 ** -11, 0.0, -0.0],
+    ])
+    for S in (127, 100, 140, 0, 254):
+        x = np.ldexp(y, S - 127)
+        ok = np.isfinite(x) & (np.ldexp(x, 127 - S) == y)  # x exactly y 2^(S-127)
+        got = oracle.quantize_f64_with_scale(x[ok], S)
+        assert np.array_equal(got, table_encode(y[ok])), S
+
+
+def test_quantize_rows_f64_equals_bf16_path_on_bf16_values():
+    rng = np.random.default_rng(23)
+    x = _random_bf16(rng, (96, 256), spread=40)
+    x[3, 32:64] = 0
+    x[4, 0:32] = rng.integers(1, 0x80, 32).astype(np.uint16)  # bf16 subnormals
+    q, s = oracle.quantize_rows(x)
+    q2, s2 = oracle.quantize_rows_f64(bf16_bits_to_f64(x))
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+
+
+def _times64_bits(x):
+    """bf16 bits of 64 x (exponent field + 6), for normal bf16 x below 2^120."""
+    e = (x >> 7) & 0xFF
+    assert np.all((e > 0) & (e < 0xF0))
+    return ((x & 0x807F) | ((e + 6) << 7)).astype(np.uint16)
+
+
+def test_swiglu_saturated_gate_reduces_to_quantize_rows():
+    """gate = 64: silu(64) = 64 exactly, so h = 64 up and its quantization is the
+    bf16 quantizer's on the bits of 64 up (a gate/up mix-up or a wrong silu
+    gives other values)."""
+    rng = np.random.default_rng(24)
+    up = _random_bf16(rng, (40, 256), spread=12)
+    up[(up >> 7) & 0xFF == 0] = 0x3F80  # keep every element a normal number
+    gate = np.full(up.shape, 64.0)
+    h, q, s = oracle.swiglu_quantize(gate, bf16_bits_to_f64(up))
+    assert np.array_equal(h, 64.0 * bf16_bits_to_f64(up))
+    q_ref, s_ref = oracle.quantize_rows(_times64_bits(up))
+    assert np.array_equal(q, q_ref) and np.array_equal(s, s_ref)
+    # zero gate: silu(0) = 0, every block is zero with scale byte 0
+    h0, q0, s0 = oracle.swiglu_quantize(np.zeros(up.shape), bf16_bits_to_f64(up))
+    assert np.all(h0 == 0) and np.all(E4M3[q0] == 0) and np.all(s0 == 0)
+
+
+def test_swiglu_quantization_invariants():
+    """Random gate/up: every nonzero block's largest |y| lies in [2^8, 2^9);
+    normal-range elements are within half an E4M3 ulp (2^-4 of their binade),
+    subnormal-range ones within half the subnormal quantum, and only |y| beyond
+    448 + 16 saturates."""
+    rng = np.random.default_rng(25)
+    gate = rng.standard_normal((64, 512)) * 3.0
+    up = rng.standard_normal((64, 512)) * np.exp2(rng.uniform(-30, 30, (64, 1)))
+    h, q, s = oracle.swiglu_quantize(gate, up)
+    Sx = np.repeat(s.astype(np.float64), 32, axis=1)
+    y = np.ldexp(h, (127 - Sx).astype(np.int64))
+    amax_y = np.abs(y).reshape(64, 16, 32).max(axis=2)
+    assert np.all((amax_y >= 256.0) & (amax_y < 512.0))
+    v = E4M3[q]
+    normal = (np.abs(y) >= 2.0 ** -6) & (np.abs(y) <= 448.0)
+    assert np.all(np.abs(v - y)[normal] <= np.exp2(np.floor(np.log2(np.abs(y[normal]))) - 4))
+    sub = np.abs(y) < 2.0 ** -6
+    assert np.all(np.abs(v - y)[sub] <= 2.0 ** -10)
+    assert np.all(np.abs(v[np.abs(y) >= 464.0]) == 448.0)
+    assert np.all(np.sign(v[v != 0]) == np.sign(y[v != 0]))
+
+
+def test_grouped_gemm_swiglu_one_hot_routing():
+    """Each row of X holds one 1.0 (column km); every gate weight is 64, so
+    gate = 64 and up = expert g's up weight at column km: the layer's output is
+    the bf16 quantizer's on 64 Wu[g][c][km], with rows past the last group
+    zero.  Pins the expert choice and the gate/up roles of the composition."""
+    rng = np.random.default_rng(26)
+    M, I, K = 48, 64, 256
+    off = np.array([0, 12, 12, 40], np.int32)  # rows 40..47 belong to no group
+    G = 3
+    km = rng.integers(0, K, M)
+    Xq = np.zeros((M, K), np.uint8)
+    Xq[np.arange(M), km] = 0x38                # 1.0
+    Xs = np.full((M, K // 32), 127, np.uint8)
+    Wgq = np.full((G, I, K), 0x38, np.uint8)
+    Wgs = np.full((G, I, K // 32), 133, np.uint8)  # 1.0 * 2^6
+    Wuq = rng.integers(0, 0x7F, (G, I, K)).astype(np.uint8) | (rng.integers(0, 2, (G, I, K)) << 7).astype(np.uint8)
+    Wuq[(Wuq & 0x7F) == 0x7F] = 0x40           # no NaN codes
+    Wuq[(Wuq & 0x7F) == 0] = 0x30              # and no zeros: up (a sum from +0) is never -0
+    Wus = rng.integers(110, 140, (G, I, K // 32)).astype(np.uint8)
+    h, q, s, gate, up = oracle.grouped_gemm_swiglu(Xq, Xs, Wgq, Wgs, Wuq, Wus, off)
+    upv = np.zeros((M, I))
+    for m in range(40):
+        g = 0 if m < 12 else 2
+        k = km[m]
+        upv[m] = E4M3[Wuq[g, :, k]] * np.exp2(Wus[g, :, k // 32].astype(np.float64) - 127)
+    assert np.all(gate[:40] == 64.0) and np.all(gate[40:] == 0.0)
+    assert np.array_equal(up, upv)
+    # 64 up is a bf16 value (3 fraction bits, exponent in range): quantize its bits
+    hb = (np.asarray(64.0 * upv, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(bf16_bits_to_f64(hb), 64.0 * upv)
+    q_ref, s_ref = oracle.quantize_rows(hb)
+    assert np.array_equal(q[:40], q_ref[:40]) and np.array_equal(s[:40], s_ref[:40])
+    assert np.all(E4M3[q[40:]] == 0) and np.all(s[40:] == 0)
+
+
+def test_grouped_gemm_swiglu_blocks_match_full():
+    rng = np.random.default_rng(27)
+    M, I, K, G = 70, 96, 128, 2
+    off = np.array([0, 33, 70], np.int32)
+    x = _random_bf16(rng, (M, K), spread=3)
+    wg = _random_bf16(rng, (G * I, K), spread=2)
+    wu = _random_bf16(rng, (G * I, K), spread=2)
+    Xq, Xs = oracle.quantize_rows(x)
+    Wgq, Wgs = oracle.quantize_rows(wg)
+    Wuq, Wus = oracle.quantize_rows(wu)
+    args = (Xq, Xs, Wgq.reshape(G, I, K), Wgs.reshape(G, I, K // 32), Wuq.reshape(G, I, K),
+            Wus.reshape(G, I, K // 32), off)
+    h, q, s, gate, up = oracle.grouped_gemm_swiglu(*args)
+    rows = np.array([0, 32, 33, 69, 5], np.int64)
+    blocks = np.array([0, 2, 1, 2, 1], np.int64)
+    hb, qb, sb, gb, ub = oracle.grouped_gemm_swiglu_blocks(*args, rows, blocks)
+    for i, (r, b) in enumerate(zip(rows, blocks)):
+        sl = slice(32 * b, 32 * b + 32)
+        assert np.array_equal(hb[i], h[r, sl]) and np.array_equal(qb[i], q[r, sl]) and sb[i] == s[r, b]
+        assert np.array_equal(gb[i], gate[r, sl]) and np.array_equal(ub[i], up[r, sl])

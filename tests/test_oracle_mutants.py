@@ -31,6 +31,12 @@ MUTANTS = {
                          "acc += mxref_dequant(xr[k], xs[k / 32]) * mxref_dequant(wr[k], ws[(k + 1) / 32]);"),
     "wgrad_skip_first": ("for (int64_t t = P[g]; t < P[g + 1]; ++t)", "for (int64_t t = P[g] + 1; t < P[g + 1]; ++t)"),
     "e4m3_bias": ("else v = ldexp((double)(8 + fr), ef - 7 - 3);", "else v = ldexp((double)(8 + fr), ef - 8 - 3);"),
+    "silu_sign": ("return x / (1.0 + exp(-x));", "return x / (1.0 + exp(x));"),
+    "swiglu_roles": ("h[i] = mxref_silu(gate[i]) * up[i];", "h[i] = mxref_silu(up[i]) * gate[i];"),
+    "f64_signed_amax": ("if (fabs(x[i]) > amax) amax = fabs(x[i]);", "if (x[i] > amax) amax = x[i];"),
+    "f64_scale_direction": ("q[i] = mxref_e4m3_encode(ldexp(x[i], 127 - (int)S));",
+                            "q[i] = mxref_e4m3_encode(ldexp(x[i], (int)S - 127));"),
+    "f64_block_stride": ("const double* blk = x + m * K + b * 32;", "const double* blk = x + m * K + b * 31;"),
 }
 
 
