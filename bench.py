@@ -17,8 +17,9 @@ element) next to the two separate passes.
 
 The ``gemm`` object times the grouped GEMMs on the MoE workloads (TFLOP/s =
 2 M N K over real rows / GPU time): gate+up (32768 x 7168 -> 4096, 16 experts),
-the ragged 128-expert case next to the dense GEMM of the same size, and the
-down projection forward / dgrad / wgrad.
+the same with the quantizing SwiGLU epilogue (MXFP8 [32768, 2048] out), the
+ragged 128-expert case next to the dense GEMM of the same size, and the down
+projection forward / dgrad / wgrad.
 
 ``roofline`` describes the dominant kernel of the step (its own launch time
 from HIP events on the launch stream); ``cpu_baseline`` times the CPU oracle
@@ -202,7 +203,27 @@ def bench_gemm(torch, mx, W, args):
     out["gate_up"] = {"M": d["M"], "N": N, "K": K, "G": G, "ms": ms, "tflops": tflops(d["M"], N, K, ms),
                       "frac_mfma_peak": tflops(d["M"], N, K, ms) / MFMA_FP8_PEAK_TFLOPS,
                       "quantize_x_ms": qx, "quantize_over_gemm": qx / ms}
-    del d, Xq, Xs, Wq, Ws, y
+    del Wq, Ws, y
+    torch.cuda.empty_cache()
+
+    # the same projection with the quantizing SwiGLU epilogue: h = silu(gate) up
+    # as MXFP8 [M, N/2] + scales instead of bf16 [M, N]
+    I = N // 2
+    Wi, Wis = mx.mx_quantize_rows(mx.swiglu_interleave(d["w"]).reshape(G * N, K))
+    Wi = Wi.reshape(G, N, K)
+    hq = torch.empty((d["M"], I), dtype=torch.uint8, device="cuda")
+    hs = torch.empty(mx.mx_scale_bytes(d["M"], I), dtype=torch.uint8, device="cuda")
+    ms_sw = timed(lambda: mx.mx_grouped_gemm_swiglu(Xq, Xs, Wi, Wis, off, hq=hq, hs=hs))
+    out["gate_up_swiglu"] = {
+        "M": d["M"], "N": N, "K": K, "G": G, "ms": ms_sw, "tflops": tflops(d["M"], N, K, ms_sw),
+        "frac_mfma_peak": tflops(d["M"], N, K, ms_sw) / MFMA_FP8_PEAK_TFLOPS,
+        "over_bf16_gemm": ms_sw / ms,
+        # bytes of the activation written by the fused kernel, and those of
+        # the unfused route (bf16 [M, N] written, read back, codes + scales written)
+        "bytes_out_fused": d["M"] * I * (1 + 1 / 32),
+        "bytes_unfused": d["M"] * N * 2 * 2 + d["M"] * I * (1 + 1 / 32),
+    }
+    del d, Xq, Xs, Wi, Wis, hq, hs
     torch.cuda.empty_cache()
 
     # ragged 128 experts vs dense

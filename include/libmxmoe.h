@@ -151,6 +151,35 @@ mx_status mx_grouped_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* W
                           int64_t N, int64_t K, uint16_t* out, void* stream);
 
 /*
+ * Gate+up grouped GEMM with a quantizing SwiGLU epilogue (the MoE layer's
+ * first projection, its activation and the MXFP8 quantization of the
+ * activation for the down projection in one pass: kucoin.com MoK page,
+ * section 02, MXFP8 fused into the SwiGLU step; aigc.bar "被忽视的量化税" on
+ * the cost of separate quantization passes).  With Y = the grouped GEMM of Xq and Wq
+ * (fp32 accumulation, as mx_grouped_gemm) over 2I output columns:
+ *   h[m][c] = silu(gate[m][c]) * up[m][c],   silu(x) = x / (1 + e^-x),
+ * where the rows of each expert's [2I][K] weights alternate 32-row blocks:
+ * rows [64 b, 64 b + 32) are the gate rows of hidden units [32 b, 32 b + 32)
+ * and rows [64 b + 32, 64 b + 64) their up rows.  h is computed in fp32 and
+ * quantized along c like mx_quantize_rows (S = max(expfield(amax) - 8, 0)
+ * on the fp32 exponent field; codes E4M3FN of h * 2^(127-S), saturated to
+ * +/-448, nearest even):
+ *   Xq, Xs  as mx_grouped_gemm (R = M, contraction K)
+ *   Wq      uint8 [G][2I][K] in the interleaved row order above, Ws its
+ *           packed scales ([G*2I][K])
+ *   hq      uint8 [M][I] codes; hs packed scales (R = M, contraction I),
+ *           ready as the X operand of the down projection
+ * Rows of a group are written once; rows outside every group, and the
+ * scale bytes of the padding rows [M, 32 ceil(M / 32)), are left untouched
+ * (no output row reads them).  Requires K % 256 == 0 and I % 128 == 0
+ * (MX_ERR_UNSUPPORTED otherwise), 1 <= G <= 4096, 16-byte aligned pointers.
+ */
+mx_status mx_grouped_gemm_swiglu(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq,
+                                 const uint8_t* Ws, const int32_t* group_offsets, int32_t G,
+                                 int64_t M, int64_t I, int64_t K, uint8_t* hq, uint8_t* hs,
+                                 void* stream);
+
+/*
  * Data-gradient grouped GEMM (M-grouped, weights read transposed; the
  * backward pass of lpnh.cn 2479732 section 1):
  *   dX[m][n] = sum_k deq(dY[m][k]) * deq(W[g(m)][k][n])

@@ -49,6 +49,8 @@ def load():
     lib.mx_quantize_dual.restype = ST
     lib.mx_grouped_gemm.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, P]
     lib.mx_grouped_gemm.restype = ST
+    lib.mx_grouped_gemm_swiglu.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, P, P]
+    lib.mx_grouped_gemm_swiglu.restype = ST
     lib.mx_grouped_gemm_dgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, I64, P, P]
     lib.mx_grouped_gemm_dgrad.restype = ST
     lib.mx_grouped_gemm_wgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, P]
@@ -60,7 +62,7 @@ def load():
 # Exported C symbols, in header order.
 SYMBOLS = (
     "mx_status_str", "mx_version", "mx_scale_bytes", "mx_cols_capacity", "mx_quantize_rows",
-    "mx_quantize_cols", "mx_quantize_dual", "mx_grouped_gemm", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad",
+    "mx_quantize_cols", "mx_quantize_dual", "mx_grouped_gemm", "mx_grouped_gemm_swiglu", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad",
 )
 
 
@@ -173,6 +175,35 @@ def mx_grouped_gemm(Xq, Xs, Wq, Ws, group_offsets, out=None, stream=None):
                                 _stream(stream))
     _check(rc, "mx_grouped_gemm")
     return out
+
+
+def swiglu_interleave(w):
+    """Row order of the gate+up weights for mx_grouped_gemm_swiglu: w [G, 2I, K]
+    with gate rows [0, I) and up rows [I, 2I) -> rows alternating 32-row gate
+    and up blocks (a view-free reordering; works on bf16 or fp8 code rows)."""
+    G, N2, K = w.shape
+    I = N2 // 2
+    gate = w[:, :I].reshape(G, I // 32, 32, K)
+    up = w[:, I:].reshape(G, I // 32, 32, K)
+    return torch.stack([gate, up], dim=2).reshape(G, N2, K)
+
+
+def mx_grouped_gemm_swiglu(Xq, Xs, Wq, Ws, group_offsets, hq=None, hs=None, stream=None):
+    """Gate+up grouped GEMM + SwiGLU + MXFP8 quantization of the result.
+    Wq uint8 [G, 2I, K] in swiglu_interleave order; returns (hq uint8 [M, I], hs packed)."""
+    M, K = Xq.shape
+    G, N2, K2 = Wq.shape
+    if K2 != K or N2 % 2:
+        raise ValueError("shape mismatch")
+    I = N2 // 2
+    if hq is None:
+        hq = torch.empty((M, I), dtype=torch.uint8, device=Xq.device)
+    if hs is None:
+        hs = torch.empty(mx_scale_bytes(M, I), dtype=torch.uint8, device=Xq.device)
+    rc = load().mx_grouped_gemm_swiglu(_ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), _ptr(group_offsets), G, M, I, K,
+                                       _ptr(hq), _ptr(hs), _stream(stream))
+    _check(rc, "mx_grouped_gemm_swiglu")
+    return hq, hs
 
 
 def mx_grouped_gemm_dgrad(dYq, dYs, WTq, WTs, group_offsets, G, out=None, stream=None):

@@ -62,6 +62,10 @@ struct GemmArgs {
     int32_t mode;  // 0: rows of X grouped (forward); 1: contraction grouped (wgrad);
                    // 2: rows grouped, weights read transposed (dgrad)
     int64_t ldb;   // mode 2: row stride of the transposed weights (their Wcap)
+    // quantizing SwiGLU epilogue (mode 0 only): hidden width I = N / 2, codes
+    // hq [M][I] and packed scales hs (R = M, contraction I)
+    uint8_t* hq;
+    uint8_t* hs;
 };
 
 // Launch-wide constants of the operand layouts.
@@ -78,7 +82,7 @@ struct Tile {
     int32_t asub, bsub;  // first tile row modulo 32 (A, B)
     int32_t nchunk;      // 256-wide contraction chunks (0: no tile)
     int32_t rows, cols;  // valid part of the output tile
-    uint16_t* out;       // output element (0, 0) of the tile
+    int64_t outoff;      // element offset of the tile's output element (0, 0)
 };
 
 __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][TM * SK];
@@ -338,7 +342,9 @@ struct Pipe {
 // The barrier at 4c + 1 also frees buffer 0 (last read at step 4c), the one
 // at 4c + 3 buffer 1 (last read at 4c + 2).  vmcnt bounds: at 4c + 1 nothing
 // was issued after stage 2c + 1, except the 32 epilogue stores of the
-// previous tile (after_epilogue); at 4c + 3 nothing after stage 2c + 2.
+// previous tile (after_epilogue; EPI_STORES of them); at 4c + 3 nothing after
+// stage 2c + 2.
+template <int EPI_STORES>
 __device__ __forceinline__ void run_chunk(Pipe& P, f32x16 (&acc)[4][4], const Ahead& X, bool after_epilogue,
                                           const Lane& Ln, const Layout& L, int w, int l, int wm, int wn,
                                           uint32_t la0, uint32_t la1, uint32_t lb0, uint32_t lb1) {
@@ -348,7 +354,7 @@ __device__ __forceinline__ void run_chunk(Pipe& P, f32x16 (&acc)[4][4], const Ah
     mfma_step<0, false>(P.F0, P.F1, 0, 1, Ln, P.sa, P.sb, acc, S2, L);
     pin_acc(acc);
     // step 4c + 1
-    if (after_epilogue) wait_vm<32>();
+    if (after_epilogue) wait_vm<EPI_STORES>();
     else wait_vm<0>();
     __syncthreads();
     issue_scales(X.rsa, X.rsb, X.asub, X.bsub, X.choff, P.gpar ^ 1, w, l, L);
@@ -384,6 +390,7 @@ __device__ __forceinline__ int64_t group_lo(const int32_t* off, int g, int64_t M
 // tile >= total).  `g` is a search cursor: the tile ids a workgroup visits
 // increase, so the group of the next tile is found by walking forward from
 // the current one.
+template <int EPI>
 __device__ __forceinline__ Tile decode_tile(const GemmArgs& a, const Layout& L, int64_t tile, int64_t total,
                                             int& g) {
     Tile T;
@@ -392,7 +399,7 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& a, const Layout& L, 
         T.asub = T.bsub = 0;
         T.nchunk = 0;
         T.rows = T.cols = 0;
-        T.out = a.out;
+        T.outoff = 0;
         return T;
     }
     while (tile_end[g] <= tile) ++g;
@@ -431,7 +438,9 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& a, const Layout& L, 
             B0 = a.B + (int64_t)g * a.K;
             Bs0 = a.Bs + ((int64_t)g * a.K / 256) * 256;
         }
-        T.out = a.out + arow0 * a.N + nt * TN;
+        // the SwiGLU epilogue needs the tile's first row and column tile
+        // apart (no 64-bit division in the kernel): it gets them packed
+        T.outoff = EPI == 1 ? (arow0 << 24) + nt : arow0 * a.N + nt * TN;
         T.rows = (int32_t)(arows < TM ? arows : TM);
         T.cols = (int32_t)((a.N - nt * TN) < TN ? (a.N - nt * TN) : TN);
     } else {
@@ -452,7 +461,7 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& a, const Layout& L, 
         brows = a.K - brow0;
         B0 = a.B;
         Bs0 = a.Bs;
-        T.out = a.out + (int64_t)g * a.N * a.K + arow0 * a.K + nt * TN;
+        T.outoff = (int64_t)g * a.N * a.K + arow0 * a.K + nt * TN;
         T.rows = (int32_t)(arows < TM ? arows : TM);
         T.cols = (int32_t)(brows < TN ? brows : TN);
     }
@@ -484,9 +493,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y) << 16);
 }
 
-__device__ __forceinline__ void epilogue16(const Tile& T, const Layout& L, f32x16 (&acc)[4][4], int wm, int wn, int h,
-                                           int r32) {
-    const i32x4 ro = make_rsrc(T.out, (uint32_t)T.rows * L.ldo * 2u);
+__device__ __forceinline__ void epilogue16(uint16_t* out, const Tile& T, const Layout& L, f32x16 (&acc)[4][4], int wm,
+                                           int wn, int h, int r32) {
+    const i32x4 ro = make_rsrc(out + T.outoff, (uint32_t)T.rows * L.ldo * 2u);
     const uint32_t zero = uni(0u);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -506,6 +515,93 @@ __device__ __forceinline__ void epilogue16(const Tile& T, const Layout& L, f32x1
                 const uint32_t off = col < T.cols ? rowoff + (uint32_t)col * 2u : 0xFFFFFFF0u;
                 bstore16(ro, off, zero, i32x4{(int)sx[0], (int)sy[0], (int)sx[1], (int)sy[1]});
             }
+    }
+}
+
+// Quantizing SwiGLU epilogue (gate+up projection followed by SwiGLU and the
+// MXFP8 quantization of its result for the down projection: kucoin.com MoK
+// page, section 02, on fusing MXFP8 into the SwiGLU step; aigc.bar
+// "被忽视的量化税").
+// The weight rows of each expert alternate 32-row gate and up blocks, so the
+// tile's MFMA blocks 2jj and 2jj + 1 of a wave are the gate and up values of
+// the same 32 hidden units and each lane holds both for its row and 16 of
+// the 32 columns (the other 16 are in lane l ^ 32):
+//   h = silu(gate) * up = gate * rcp(1 + exp(-gate)) * up       (fp32;
+//   hardware exp2 and reciprocal, each within about one ulp)
+// then per row and 32 hidden units (one block along the contraction of the
+// down projection): amax over both lanes, S = max(expfield(amax) - 8, 0)
+// (the same rule as the quantize kernels, on the fp32 exponent field),
+// codes = E4M3(clamp(h * 2^(127 - S), +-448)), round to nearest even.
+// Per wave: 32 four-byte code stores and 8 one-byte scale stores, all
+// issued (rows past the tile and the half of the lanes that does not own
+// the scale get offsets outside the descriptors).
+constexpr int kSwigluStores = 40;
+
+__device__ __forceinline__ float silu(float x) {
+    return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.44269504088896341f));
+}
+
+__device__ __forceinline__ void bstore4(const i32x4& rs, uint32_t voff, uint32_t soff, uint32_t v) {
+    asm volatile("buffer_store_dword %0, %1, %2, %3 offen" ::"v"(v), "v"(voff), "s"(rs), "s"(soff) : "memory");
+}
+__device__ __forceinline__ void bstore1(const i32x4& rs, uint32_t voff, uint32_t soff, uint32_t v) {
+    asm volatile("buffer_store_byte %0, %1, %2, %3 offen" ::"v"(v), "v"(voff), "s"(rs), "s"(soff) : "memory");
+}
+
+__device__ __forceinline__ void epilogue_swiglu(const GemmArgs& a, const Tile& T, f32x16 (&acc)[4][4], int wm, int wn,
+                                                int h, int r32) {
+    const int64_t I = a.N / 2;
+    const int64_t KBh = 8 * ((I + 255) / 256);
+    // the tile's first row and first hidden column (column tile nt covers
+    // hidden columns [128 nt, 128 nt + 128))
+    const int64_t row0 = T.outoff >> 24;
+    const int64_t hcol0 = (T.outoff & 0xFFFFFF) * (TN / 2);
+    const i32x4 rq = make_rsrc(a.hq + row0 * I + hcol0, (uint32_t)((int64_t)T.rows * I));
+    const int64_t hs_bytes = ((a.M + 31) / 32) * 32 * KBh;
+    const i32x4 rsc = make_rsrc(a.hs, (uint32_t)hs_bytes);
+    const uint32_t zero = uni(0u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = wm * 128 + i * 32 + r32;
+        const int64_t grow = row0 + row;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            float hv[16];
+            float m = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                hv[e] = silu(acc[i][2 * jj][e]) * acc[i][2 * jj + 1][e];
+                m = __builtin_fmaxf(m, __builtin_fabsf(hv[e]));
+            }
+            {
+                // amax over the 32 columns: lanes l and l ^ 32 hold the two halves
+                const auto pm = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, m),
+                                                                  __builtin_bit_cast(uint32_t, m), false, false);
+                m = __builtin_fmaxf(__builtin_bit_cast(float, (uint32_t)pm[0]),
+                                    __builtin_bit_cast(float, (uint32_t)pm[1]));
+            }
+            const int E = (int)((__builtin_bit_cast(uint32_t, m) >> 23) & 0xFF);
+            const uint32_t S = (uint32_t)(E > 8 ? E - 8 : 0);
+            const float sc = __builtin_bit_cast(float, (254u - S) << 23);  // 2^(127 - S)
+            const int hcol = wn * 64 + jj * 32 + 4 * h;                       // + 8 q
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float y[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) y[u] = __builtin_fminf(__builtin_fmaxf(hv[4 * q + u] * sc, -448.0f), 448.0f);
+                int c = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+                c = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], c, true);
+                const uint32_t off = row < T.rows ? (uint32_t)((int64_t)row * I + hcol + 8 * q) : 0xFFFFFFF0u;
+                bstore4(rq, off, zero, (uint32_t)c);
+            }
+            // scale byte of (grow, block (hcol0 + wn 64 + 32 jj) / 32), from lanes 0-31
+            const int64_t b = (hcol0 + wn * 64 + jj * 32) / 32;
+            const uint32_t soff = (row < T.rows && h == 0)
+                                      ? (uint32_t)((grow >> 5) * 32 * KBh + (b >> 3) * 256 +
+                                                   unit_byte((uint32_t)(grow & 31), (uint32_t)(b & 7)))
+                                      : 0xFFFFFFF0u;
+            bstore1(rsc, soff, zero, S);
+        }
     }
 }
 
@@ -531,8 +627,10 @@ __device__ __forceinline__ void epilogue_any(uint16_t* out, int rows, int cols, 
 }
 
 // VEC16: output rows are 16-byte aligned (ldo % 8 == 0): 16-byte epilogue.
-template <bool VEC16>
+// EPI 1: quantizing SwiGLU epilogue instead of bf16 output (mode 0).
+template <bool VEC16, int EPI>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs a) {
+    constexpr int kEpiWait = EPI == 1 ? kSwigluStores : (VEC16 ? 32 : 0);
     const int t = threadIdx.x;
     const int w = t >> 6;
     const int l = t & 63;
@@ -638,7 +736,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs a) {
     const uint32_t lb0 = uni(lds_addr(lds_b[0]) + w * 64 * SK), lb1 = uni(lds_addr(lds_b[1]) + w * 64 * SK);
 
     int gcur = 0;
-    Tile T = decode_tile(a, L, tile, total, gcur);
+    Tile T = decode_tile<EPI>(a, L, tile, total, gcur);
 
     // Prologue: scales of chunk 0 into parity 0, stages 0 and 1 into buffers
     // 0 and 1; wait for the scales and stage 0.
@@ -677,15 +775,18 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs a) {
         for (; c + 1 < T.nchunk; ++c) {
             const Ahead X{T.ra, T.rb, T.rsa, T.rsb, T.asub, T.bsub, uni((uint32_t)(c + 1) * 256u),
                           uni((uint32_t)(2 * c + 2) * SK), uni((uint32_t)(2 * c + 3) * SK)};
-            run_chunk(P, acc, X, c == 0 && !first && VEC16, Ln, L, w, l, wm, wn, la0, la1, lb0, lb1);
+            run_chunk<kEpiWait>(P, acc, X, c == 0 && !first && kEpiWait > 0, Ln, L, w, l, wm, wn, la0, la1, lb0,
+                                lb1);
         }
-        const Tile Tn = decode_tile(a, L, tile + nwg, total, gcur);
+        const Tile Tn = decode_tile<EPI>(a, L, tile + nwg, total, gcur);
         {
             const Ahead X{Tn.ra, Tn.rb, Tn.rsa, Tn.rsb, Tn.asub, Tn.bsub, uni(0u), uni(0u), uni((uint32_t)SK)};
-            run_chunk(P, acc, X, c == 0 && !first && VEC16, Ln, L, w, l, wm, wn, la0, la1, lb0, lb1);
+            run_chunk<kEpiWait>(P, acc, X, c == 0 && !first && kEpiWait > 0, Ln, L, w, l, wm, wn, la0, la1, lb0,
+                                lb1);
         }
-        if (VEC16) epilogue16(T, L, acc, wm, wn, h, r32);
-        else epilogue_any(T.out, T.rows, T.cols, L.ldo, acc, wm, wn, h, r32);
+        if (EPI == 1) epilogue_swiglu(a, T, acc, wm, wn, h, r32);
+        else if (VEC16) epilogue16(a.out, T, L, acc, wm, wn, h, r32);
+        else epilogue_any(a.out + T.outoff, T.rows, T.cols, L.ldo, acc, wm, wn, h, r32);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -717,9 +818,9 @@ int num_cus() {
 void launch(const GemmArgs& a, int64_t nwg, hipStream_t stream) {
     const int64_t ldo = a.mode == 1 ? a.K : a.N;
     if (ldo % 8 == 0)
-        hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3((unsigned)nwg), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((grouped_gemm_kernel<true, 0>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3((unsigned)nwg), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((grouped_gemm_kernel<false, 0>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
 }
 
 int64_t scale_bytes(int64_t R, int64_t K) { return ((R + 31) / 32) * 32 * (8 * ((K + 255) / 256)); }
@@ -730,7 +831,7 @@ hipError_t launch_grouped_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8
                                const uint8_t* Ws, const int32_t* group_offsets, int32_t G, int64_t M,
                                int64_t N, int64_t K, uint16_t* out, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
-    GemmArgs a;
+    GemmArgs a = {};
     a.A = Xq;
     a.As = Xs;
     a.B = Wq;
@@ -753,11 +854,40 @@ hipError_t launch_grouped_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8
     return hipGetLastError();
 }
 
+hipError_t launch_grouped_gemm_swiglu(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
+                                      const int32_t* group_offsets, int32_t G, int64_t M, int64_t I, int64_t K,
+                                      uint8_t* hq, uint8_t* hs, hipStream_t stream) {
+    if (M == 0 || I == 0) return hipSuccess;
+    GemmArgs a = {};
+    a.A = Xq;
+    a.As = Xs;
+    a.B = Wq;
+    a.Bs = Ws;
+    a.offsets = group_offsets;
+    a.out = nullptr;
+    a.M = M;
+    a.N = 2 * I;
+    a.K = K;
+    a.Mcap = 0;
+    a.a_scale_bytes = scale_bytes(M, K);
+    a.b_scale_bytes = scale_bytes((int64_t)G * 2 * I, K);
+    a.G = G;
+    a.mode = 0;
+    a.ldb = 0;
+    a.hq = hq;
+    a.hs = hs;
+    const int64_t ub = ((M + TM - 1) / TM + G) * ((2 * I + TN - 1) / TN);
+    int64_t nwg = num_cus();
+    if (ub < nwg) nwg = ub;
+    hipLaunchKernelGGL((grouped_gemm_kernel<true, 1>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_grouped_gemm_dgrad(const uint8_t* dYq, const uint8_t* dYs, const uint8_t* WTq,
                                      const uint8_t* WTs, const int32_t* group_offsets, int32_t G, int64_t M,
                                      int64_t N, int64_t K, int64_t Wcap, uint16_t* dX, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
-    GemmArgs a;
+    GemmArgs a = {};
     a.A = dYq;
     a.As = dYs;
     a.B = WTq;
@@ -785,7 +915,7 @@ hipError_t launch_grouped_gemm_wgrad(const uint8_t* A, const uint8_t* As, const 
                                      int64_t N, int64_t K, int64_t Mcap, uint16_t* dW,
                                      hipStream_t stream) {
     if (N == 0 || K == 0 || G == 0) return hipSuccess;
-    GemmArgs a;
+    GemmArgs a = {};
     a.A = A;
     a.As = As;
     a.B = B;

@@ -21,6 +21,10 @@ hipError_t launch_grouped_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8
                                const uint8_t* Ws, const int32_t* group_offsets, int32_t G, int64_t M,
                                int64_t N, int64_t K, uint16_t* out, hipStream_t stream);
 
+hipError_t launch_grouped_gemm_swiglu(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
+                                      const int32_t* group_offsets, int32_t G, int64_t M, int64_t I, int64_t K,
+                                      uint8_t* hq, uint8_t* hs, hipStream_t stream);
+
 hipError_t launch_grouped_gemm_dgrad(const uint8_t* dYq, const uint8_t* dYs, const uint8_t* WTq,
                                      const uint8_t* WTs, const int32_t* group_offsets, int32_t G, int64_t M,
                                      int64_t N, int64_t K, int64_t Wcap, uint16_t* dX, hipStream_t stream);

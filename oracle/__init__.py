@@ -306,8 +306,8 @@ def grouped_gemm_swiglu(Xq, Xs, Wgq, Wgs, Wuq, Wus, offsets):
 
 def grouped_gemm_swiglu_blocks(Xq, Xs, Wgq, Wgs, Wuq, Wus, offsets, rows, blocks):
     """The same at sampled 32-wide blocks: for each (rows[i], blocks[i]) the
-    hidden units [32 b, 32 b + 32) of that row.  Returns (h, codes, gate, up)
-    as [n, 32] and scales [n]."""
+    hidden units [32 b, 32 b + 32) of that row.  Returns (h, codes, scales,
+    gate, up): h, codes, gate and up [n, 32], scales [n]."""
     rows = np.asarray(rows, np.int64)
     blocks = np.asarray(blocks, np.int64)
     r = np.repeat(rows, 32)

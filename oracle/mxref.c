@@ -282,7 +282,7 @@ void mxref_wgrad_points(const uint8_t* Aq, const uint8_t* As, const uint8_t* Bq,
 
 /* ---- SwiGLU of the gate and up projections, quantized to MXFP8 ----
  * The pages fuse the MXFP8 quantization of the activation into the SwiGLU
- * step of the MoE layer (kucoin.com MoK page; aigc.bar "被忽视的量化税" on
+ * step of the MoE layer (kucoin.com MoK page, section 02; aigc.bar "被忽视的量化税" on
  * the cost of a separate quantization pass).  They give no formula.  Readings
  * taken here:
  *   - SwiGLU(gate, up) = silu(gate) * up with silu(x) = x * sigmoid(x) =

@@ -101,6 +101,21 @@ def test_grouped_gemm_validation():
     assert f(None, None, None, None, None, 4, 0, 128, 256, None, None) == 0    # M == 0: no work
 
 
+def test_grouped_gemm_swiglu_validation():
+    f = mx.load().mx_grouped_gemm_swiglu
+    # (Xq, Xs, Wq, Ws, offsets, G, M, I, K, hq, hs, stream)
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 2048, 288, FAKE, FAKE, None) == 5   # K % 256 != 0
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 192, 512, FAKE, FAKE, None) == 5   # I % 128 != 0
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 2048, 250, FAKE, FAKE, None) == 2  # K % 32 != 0
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 512, 2048, 512, FAKE, FAKE, None) == 2  # G < 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, -1, 2048, 512, FAKE, FAKE, None) == 2   # M < 0
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 2048, 512, None, FAKE, None) == 1  # NULL hq
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 2048, 512, FAKE, None, None) == 1  # NULL hs
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 2048, 512, FAKE, P(0x100001), None) == 3  # misaligned hs
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 1 << 22, 512, FAKE, FAKE, None) == 5  # 2I past the limit
+    assert f(None, None, None, None, None, 4, 0, 2048, 512, None, None, None) == 0    # M == 0: no work
+
+
 def test_dgrad_validation():
     f = mx.load().mx_grouped_gemm_dgrad
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 64, 512, 1024, FAKE, None) == 4   # Wcap < G*K

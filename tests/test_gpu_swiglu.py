@@ -1,0 +1,215 @@
+"""GPU parity of mx_grouped_gemm_swiglu (gate+up grouped GEMM, SwiGLU and the
+MXFP8 quantization of its result in one kernel) against the fp64 oracle.
+
+The kernel accumulates the projections in fp32 and evaluates silu in fp32,
+so its h differs from the oracle's fp64 h by at most a radius e derived
+below from sum |x| |w|.  The check is then exact in both directions:
+  - every scale byte lies in [S(amax_lo), S(amax_hi)], the scales of the
+    smallest and largest block amax that h +/- e allows;
+  - every code's value lies between the oracle encodings of (h - e) and
+    (h + e) under the kernel's own scale byte (encoding is monotone).
+Elements clear of a rounding boundary must therefore match exactly; on top
+of that, all but a small fraction of codes and scales must equal the
+oracle's, which a wrong rounding mode or scale rule would break.
+
+Error radius (fp32 unit roundoff u = 2^-24; A_g = sum_k |x_k| |w_k|):
+  |g - g_ref| <= dg = (2^-16 + (K / 64) u) A_g, same for up.  The scaled
+      MFMA's internal precision is not documented; the model takes each
+      64-deep step to sum its products to at least 16 significant bits of
+      their magnitude sum, plus one fp32 rounding of the accumulator per
+      step.  The largest error measured on this hardware (up to 2^-17.5 A on
+      K = 256, from codes that could only come from such an error) is about
+      a third of the model;
+  silu in fp32: g * rcp(1 + exp2(-g log2 e)), relative error <= (|g| + 6) u;
+      |silu'| <= 1.1;
+  e = 2 (|s| du + 1.1 |u| dg + 1.1 dg du + |h| (|g| + 8) u) + 2^-130.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_block_scaled_04_amd as mx
+import oracle
+from mxfp8_block_scaled_04_amd import workloads as W
+from tests.mxtest import canonical_scales, u8
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+FILL = 0xEE
+E4M3 = np.array([oracle.e4m3_value(c) for c in range(256)])
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    mx.load()
+
+
+def run_swiglu(x, w, offsets):
+    """x bf16 [M, K]; w bf16 [G, 2I, K] with gate rows [0, I) and up rows
+    [I, 2I).  Quantizes both on the GPU, runs the fused kernel into outputs
+    prefilled with FILL; returns device outputs and host oracle operands."""
+    M, K = x.shape
+    G, N2, _ = w.shape
+    I = N2 // 2
+    wi = mx.swiglu_interleave(w)
+    # the interleaved order: rows [64 b, 64 b + 32) gate block b, then its up block
+    wi4 = wi.reshape(G, I // 32, 2, 32, K)
+    assert torch.equal(wi4[:, :, 0], w[:, :I].reshape(G, I // 32, 32, K))
+    assert torch.equal(wi4[:, :, 1], w[:, I:].reshape(G, I // 32, 32, K))
+    Xq, Xs = mx.mx_quantize_rows(x)
+    Wq, Ws = mx.mx_quantize_rows(wi.reshape(G * N2, K))
+    hq = torch.full((M, I), FILL, dtype=torch.uint8, device=DEV)
+    hs = torch.full((mx.mx_scale_bytes(M, I),), FILL, dtype=torch.uint8, device=DEV)
+    off_dev = torch.from_numpy(offsets).to(DEV)
+    mx.mx_grouped_gemm_swiglu(Xq, Xs, Wq.reshape(G, N2, K), Ws, off_dev, hq=hq, hs=hs)
+    torch.cuda.synchronize()
+    # host operands in the oracle's terms: separate gate and up weights
+    hx, hxs = u8(Xq), canonical_scales(Xs, M, K)
+    wq = u8(Wq).reshape(G, I // 32, 2, 32, K)
+    ws = canonical_scales(Ws, G * N2, K).reshape(G, I // 32, 2, 32, K // 32)
+    Wgq = np.ascontiguousarray(wq[:, :, 0].reshape(G, I, K))
+    Wuq = np.ascontiguousarray(wq[:, :, 1].reshape(G, I, K))
+    Wgs = np.ascontiguousarray(ws[:, :, 0].reshape(G, I, K // 32))
+    Wus = np.ascontiguousarray(ws[:, :, 1].reshape(G, I, K // 32))
+    return hq, hs, (hx, hxs, Wgq, Wgs, Wuq, Wus)
+
+
+def abs_codes(q):
+    return q & np.uint8(0x7F)
+
+
+def error_radius(h, gate, up, Ag, Au, K):
+    u = 2.0 ** -24
+    dg = (2.0 ** -16 + K / 64 * u) * Ag
+    du = (2.0 ** -16 + K / 64 * u) * Au
+    s = gate / (1.0 + np.exp(-np.clip(gate, -700.0, 700.0)))
+    e = np.abs(s) * du + 1.1 * np.abs(up) * dg + 1.1 * dg * du + np.abs(h) * (np.abs(gate) + 8.0) * u
+    return 2.0 * e + 2.0 ** -130
+
+
+def check_blocks(q_gpu, s_gpu, h, gate, up, Ag, Au, K, min_exact_codes=0.995, min_exact_scales=0.999):
+    """q_gpu [n, 32] codes and s_gpu [n] scale bytes of n blocks against the
+    oracle's h, gate, up [n, 32] and abs sums Ag, Au [n, 32]."""
+    assert not np.any((q_gpu & 0x7F) == 0x7F), "NaN code"
+    e = error_radius(h, gate, up, Ag, Au, K)
+    lo, hi = h - e, h + e
+    amax_lo = np.max(np.maximum(np.abs(h) - e, 0.0), axis=1)
+    amax_hi = np.max(np.abs(h) + e, axis=1)
+    s_lo = np.array([oracle.block_scale_f64(np.array([a])) for a in amax_lo])
+    s_hi = np.array([oracle.block_scale_f64(np.array([a])) for a in amax_hi])
+    bad_s = np.nonzero((s_gpu < s_lo) | (s_gpu > s_hi))[0]
+    assert bad_s.size == 0, f"scale outside its interval in block {bad_s[0]}: {s_gpu[bad_s[0]]} not in [{s_lo[bad_s[0]]}, {s_hi[bad_s[0]]}]"
+    v = E4M3[q_gpu]
+    for i in range(q_gpu.shape[0]):
+        S = int(s_gpu[i])
+        vlo = E4M3[oracle.quantize_f64_with_scale(lo[i], S)]
+        vhi = E4M3[oracle.quantize_f64_with_scale(hi[i], S)]
+        bad = np.nonzero((v[i] < vlo) | (v[i] > vhi))[0]
+        assert bad.size == 0, (f"block {i} element {bad[0]}: code {q_gpu[i, bad[0]]:#x} outside "
+                               f"[{vlo[bad[0]]}, {vhi[bad[0]]}] for h = {h[i, bad[0]]!r}, S = {S}")
+    h_ref, q_ref, s_ref = oracle.swiglu_quantize(gate, up)
+    s_ref = s_ref[:, 0]  # one block per row here
+    exact_s = float(np.mean(s_gpu == s_ref))
+    same = s_gpu == s_ref
+    exact_q = float(np.mean(E4M3[q_gpu[same]] == E4M3[q_ref[same]])) if same.any() else 1.0
+    print(f"blocks {q_gpu.shape[0]}: exact scales {exact_s:.5f}, exact codes (same scale) {exact_q:.5f}")
+    assert exact_s >= min_exact_scales and exact_q >= min_exact_codes, (exact_s, exact_q)
+
+
+def full_check(x, w, sizes):
+    M, K = x.shape
+    G, N2, _ = w.shape
+    I = N2 // 2
+    off = W.offsets_from_sizes(sizes)
+    hq, hs, ops = run_swiglu(x, w, off)
+    h, q_ref, s_ref, gate, up = oracle.grouped_gemm_swiglu(*ops, off)
+    hx, hxs, Wgq, Wgs, Wuq, Wus = ops
+    Ag = oracle.grouped_gemm(abs_codes(hx), hxs, abs_codes(Wgq), Wgs, off)
+    Au = oracle.grouped_gemm(abs_codes(hx), hxs, abs_codes(Wuq), Wus, off)
+    q = u8(hq)
+    hs_h = u8(hs)
+    Mpad = 32 * ((M + 31) // 32)
+    s = oracle.unpack_scales(hs_h, M, I)
+    lo, hi = int(off[0]), int(off[-1])
+    rows = np.arange(lo, hi)
+    nb = I // 32
+    blk = lambda a: a[rows].reshape(-1, nb, 32).reshape(-1, 32)
+    check_blocks(blk(q), s[rows].reshape(-1), blk(h), blk(gate), blk(up), blk(Ag), blk(Au), K)
+    # rows outside every group and the padding rows' scale bytes are untouched
+    outside = np.r_[0:lo, hi:M]
+    assert np.all(q[outside] == FILL) and np.all(s[outside] == FILL)
+    if Mpad > M:
+        probe = np.zeros((Mpad, nb), np.uint8)
+        probe[M:] = 1
+        assert np.all(hs_h[oracle.pack_scales(probe, I) == 1] == FILL)
+
+
+@pytest.mark.parametrize("sizes,I,K", [
+    ([100, 0, 37, 300, 163], 256, 512),
+    ([1, 31, 33, 0, 257, 5], 128, 256),
+    ([513], 384, 768),
+    ([0, 0, 64], 128, 256),
+])
+def test_swiglu_full(sizes, I, K):
+    M, G = sum(sizes), len(sizes)
+    x = W.normal_bf16((M, K), 1.0, 100 + M, DEV)
+    w = W.normal_bf16((G, 2 * I, K), 1.2 / np.sqrt(K), 200 + K, DEV)
+    full_check(x, w, sizes)
+
+
+def test_swiglu_rows_outside_groups_zero_rows_and_scaled_rows():
+    """Groups cover rows [16, 150) of 170; some rows are all zero (h = 0,
+    scale byte 0) and row magnitudes spread over 2^-8 .. 2^8."""
+    M, I, K, G = 170, 256, 512, 3
+    sizes = [60, 0, 74]
+    x = W.normal_bf16((M, K), 1.0, 7, DEV).float()
+    x *= torch.exp2(torch.linspace(-8, 8, M, device=DEV)).unsqueeze(1)
+    x[20] = 0
+    x[100] = 0
+    x = x.to(torch.bfloat16)
+    w = W.normal_bf16((G, 2 * I, K), 1.2 / np.sqrt(K), 8, DEV)
+    off = np.array([16, 76, 76, 150], np.int32)
+    hq, hs, ops = run_swiglu(x, w, off)
+    h, q_ref, s_ref, gate, up = oracle.grouped_gemm_swiglu(*ops, off)
+    hx, hxs, Wgq, Wgs, Wuq, Wus = ops
+    Ag = oracle.grouped_gemm(abs_codes(hx), hxs, abs_codes(Wgq), Wgs, off)
+    Au = oracle.grouped_gemm(abs_codes(hx), hxs, abs_codes(Wuq), Wus, off)
+    q, s = u8(hq), oracle.unpack_scales(u8(hs), M, I)
+    rows = np.arange(16, 150)
+    blk = lambda a: a[rows].reshape(-1, 32)
+    check_blocks(blk(q), s[rows].reshape(-1), blk(h), blk(gate), blk(up), blk(Ag), blk(Au), K)
+    assert np.all(E4M3[q[20]] == 0) and np.all(s[20] == 0)
+    assert np.all(q[:16] == FILL) and np.all(q[150:] == FILL)
+    assert np.all(s[:16] == FILL) and np.all(s[150:] == FILL)
+
+
+def test_swiglu_gate_up_sampled():
+    """The MoE gate+up workload (32768 rows, K = 7168, I = 2048, 16 experts),
+    in the launch configuration the benchmark times: sampled 32-wide blocks
+    (uniform, plus the first and last rows of every group)."""
+    d = W.moe_gate_up(seed=0, device=DEV)
+    M, K, G = d["M"], d["K"], d["G"]
+    I = d["N"] // 2
+    off = d["offsets"]
+    hq, hs, ops = run_swiglu(d["x"], d["w"], off)
+    rng = np.random.default_rng(5)
+    rows = list(rng.integers(0, M, 384))
+    blocks = list(rng.integers(0, I // 32, 384))
+    for g in range(G):
+        lo, hi = int(off[g]), int(off[g + 1])
+        if hi > lo:
+            for r in (lo, hi - 1):
+                rows += [r, r]
+                blocks += [0, I // 32 - 1]
+    rows = np.array(rows, np.int64)
+    blocks = np.array(blocks, np.int64)
+    h, q_ref, s_ref, gate, up = oracle.grouped_gemm_swiglu_blocks(*ops, off, rows, blocks)
+    hx, hxs, Wgq, Wgs, Wuq, Wus = ops
+    # sums of |x| |w|: the same blocks over the magnitudes of the codes
+    _, _, _, Ag, Au = oracle.grouped_gemm_swiglu_blocks(abs_codes(hx), hxs, abs_codes(Wgq), Wgs, abs_codes(Wuq), Wus,
+                                                        off, rows, blocks)
+    q = u8(hq)
+    s = oracle.unpack_scales(u8(hs), M, I)
+    cols = blocks[:, None] * 32 + np.arange(32)[None, :]
+    check_blocks(q[rows[:, None], cols], s[rows, blocks], h, gate, up, Ag, Au, K)

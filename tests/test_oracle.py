@@ -452,7 +452,7 @@ def test_wgrad_matches_rowwise_gemm_of_padded_slices():
 
 # ---------------------------------------------------------------------------
 # SwiGLU of the gate and up projections, quantized to MXFP8 (the activation
-# step of the MoE layer that the kucoin.com MoK page fuses with the
+# step of the MoE layer that the kucoin.com MoK page (section 02) fuses with the
 # quantization): closed forms of silu, a closed-form scale sweep on real
 # values, the table-search encoder on off-grid values, and reductions to the
 # pinned bf16 quantizer.
