@@ -30,6 +30,12 @@ Parity status of each function (what pins it in ``tests/test_oracle.py``):
                                      zero gate, quantization-error invariants
   grouped_gemm_swiglu(_blocks)       one-hot routing closed form (expert and
                                      gate/up roles), full vs sampled agreement
+  dsilu                              closed forms (0, ln 3, large |x|), central
+                                     differences of silu
+  bf16_round                         torch's float32 -> bf16 conversion on
+                                     float32 values, hand-worked ties, values
+                                     past float32 precision (no double rounding)
+  swiglu_backward                    zero and saturated gates in closed form
 """
 import ctypes
 import os
@@ -96,6 +102,11 @@ def _load():
     lib.mxref_quantize_f64_with_scale.argtypes = [P, I64, ctypes.c_uint8, P]
     lib.mxref_quantize_rows_f64.argtypes = [P, I64, I64, P, P]
     lib.mxref_swiglu_quantize.argtypes = [P, P, I64, I64, P, P, P]
+    lib.mxref_dsilu.argtypes = [ctypes.c_double]
+    lib.mxref_dsilu.restype = ctypes.c_double
+    lib.mxref_bf16_round.argtypes = [ctypes.c_double]
+    lib.mxref_bf16_round.restype = ctypes.c_uint16
+    lib.mxref_swiglu_backward.argtypes = [P, P, P, I64, P, P, P]
     _lib = lib
     return lib
 
@@ -316,3 +327,25 @@ def grouped_gemm_swiglu_blocks(Xq, Xs, Wgq, Wgs, Wuq, Wus, offsets, rows, blocks
     up = grouped_gemm_points(Xq, Xs, Wuq, Wus, offsets, r, c).reshape(-1, 32)
     h, q, s = swiglu_quantize(gate, up)
     return h, q, s[:, 0], gate, up
+
+
+def dsilu(x):
+    return _load().mxref_dsilu(float(x))
+
+
+def bf16_round(x):
+    """double array -> bf16 bit patterns (uint16), nearest even, one rounding."""
+    a = np.asarray(x, np.float64)
+    f = _load().mxref_bf16_round
+    return np.array([f(float(v)) for v in a.reshape(-1)], np.uint16).reshape(a.shape)
+
+
+def swiglu_backward(gate, up, dh):
+    """gate, up, dh double arrays of one shape -> (dgate, dup, h) in double."""
+    g, pg = _c(gate, np.float64)
+    u, pu = _c(up, np.float64)
+    d, pd = _c(dh, np.float64)
+    assert g.shape == u.shape == d.shape
+    out = [np.empty(g.shape, np.float64) for _ in range(3)]
+    _load().mxref_swiglu_backward(pg, pu, pd, g.size, *[o.ctypes.data_as(ctypes.c_void_p) for o in out])
+    return tuple(out)

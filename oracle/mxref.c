@@ -324,3 +324,48 @@ void mxref_swiglu_quantize(const double* gate, const double* up, int64_t M, int6
     for (int64_t i = 0; i < M * I; ++i) h[i] = mxref_silu(gate[i]) * up[i];
     mxref_quantize_rows_f64(h, M, I, q, s);
 }
+
+/* ---- Backward pass of SwiGLU ----
+ * Readings (the pages give no formula; this is the derivative of the
+ * forward reading above, term by term):
+ *   sigma(g) = 1 / (1 + e^-g), silu'(g) = sigma(g) (1 + g (1 - sigma(g)));
+ *   d gate = dh * up * silu'(gate), d up = dh * silu(gate), and the
+ *   activation h = silu(gate) * up, all in double;
+ *   results stored as bf16: round to nearest, ties to even, directly from
+ *   the double value (one rounding), overflow to infinity.
+ */
+double mxref_dsilu(double x) {
+    double sig = 1.0 / (1.0 + exp(-x));
+    return sig * (1.0 + x * (1.0 - sig));
+}
+
+uint16_t mxref_bf16_round(double x) {
+    require_rne();
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (a == 0.0) return sign;
+    int e;
+    (void)frexp(a, &e);
+    int E = e - 1;                                    /* floor(log2 a) */
+    if (E < -126) {
+        /* subnormal range: multiples of 2^-133 (128 of them reach 2^-126) */
+        int n = (int)nearbyint(ldexp(a, 133));
+        return (uint16_t)(sign | n);                  /* n = 128 is the smallest normal */
+    }
+    double n = nearbyint(ldexp(a, 7 - E));            /* 128..256 */
+    if (n == 256.0) {
+        n = 128.0;
+        E += 1;
+    }
+    if (E > 127) return (uint16_t)(sign | 0x7F80);    /* infinity */
+    return (uint16_t)(sign | ((E + 127) << 7) | ((int)n - 128));
+}
+
+void mxref_swiglu_backward(const double* gate, const double* up, const double* dh, int64_t n, double* dgate,
+                           double* dup, double* h) {
+    for (int64_t i = 0; i < n; ++i) {
+        dgate[i] = dh[i] * up[i] * mxref_dsilu(gate[i]);
+        dup[i] = dh[i] * mxref_silu(gate[i]);
+        h[i] = mxref_silu(gate[i]) * up[i];
+    }
+}

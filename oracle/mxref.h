@@ -107,6 +107,12 @@ void mxref_quantize_rows_f64(const double* x, int64_t M, int64_t K, uint8_t* q, 
 void mxref_swiglu_quantize(const double* gate, const double* up, int64_t M, int64_t I, double* h, uint8_t* q,
                            uint8_t* s);
 
+/* SwiGLU backward (readings in mxref.c); all arrays of n doubles. */
+double mxref_dsilu(double x);
+uint16_t mxref_bf16_round(double x);
+void mxref_swiglu_backward(const double* gate, const double* up, const double* dh, int64_t n, double* dgate,
+                           double* dup, double* h);
+
 #ifdef __cplusplus
 }
 #endif

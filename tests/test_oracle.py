@@ -628,3 +628,74 @@ def test_grouped_gemm_swiglu_blocks_match_full():
         sl = slice(32 * b, 32 * b + 32)
         assert np.array_equal(hb[i], h[r, sl]) and np.array_equal(qb[i], q[r, sl]) and sb[i] == s[r, b]
         assert np.array_equal(gb[i], gate[r, sl]) and np.array_equal(ub[i], up[r, sl])
+
+
+# ---------------------------------------------------------------------------
+# Backward pass of SwiGLU: closed forms, central differences, and the bf16
+# rounding of the results against torch's conversion and hand-worked ties.
+# ---------------------------------------------------------------------------
+
+
+def test_dsilu_closed_forms():
+    ln3 = math.log(3.0)
+    assert oracle.dsilu(0.0) == 0.5
+    # sigma(ln 3) = 3/4: silu'(ln 3) = 3/4 (1 + ln 3 / 4); sigma(-ln 3) = 1/4
+    assert _ulps(oracle.dsilu(ln3), 0.75 * (1.0 + 0.25 * ln3)) <= 8
+    assert _ulps(oracle.dsilu(-ln3), 0.25 * (1.0 - 0.75 * ln3)) <= 64
+    assert oracle.dsilu(64.0) == 1.0
+    assert -64.0 * 2.0 ** -90 < oracle.dsilu(-64.0) < 0.0
+    assert oracle.dsilu(-1000.0) == 0.0
+
+
+def test_dsilu_central_differences():
+    rng = np.random.default_rng(30)
+    d = 1e-5
+    for x in rng.uniform(-20.0, 20.0, 300):
+        fd = (oracle.silu(x + d) - oracle.silu(x - d)) / (2 * d)
+        assert abs(fd - oracle.dsilu(x)) <= 1e-8, x
+
+
+def test_bf16_round_matches_torch_on_float32_values():
+    import torch
+    rng = np.random.default_rng(31)
+    f = (rng.standard_normal(20000) * np.exp2(rng.uniform(-140, 128, 20000))).astype(np.float32)
+    # exact midpoints between neighbouring bf16 values (representable in float32)
+    b = (rng.integers(0, 0x7F7F, 4000).astype(np.uint32) << 16)
+    mids = (b | 0x8000).view(np.float32)
+    f = np.concatenate([f, mids, -mids, np.array([0.0, -0.0, 3.3895e38, 1e-45], np.float32)])
+    f = f[np.isfinite(f)]
+    want = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.bf16_round(f.astype(np.float64)), want)
+
+
+def test_bf16_round_ties_and_single_rounding():
+    # 1 + 2^-8 lies halfway between 1 (even) and 1 + 2^-7; 1 + 3 2^-8 between
+    # 1 + 2^-7 (odd) and 1 + 2^-6 (even)
+    assert oracle.bf16_round(1 + 2.0 ** -8) == 0x3F80
+    assert oracle.bf16_round(1 + 3 * 2.0 ** -8) == 0x3F82
+    # just past the midpoint by less than float32 can hold: rounding through
+    # float32 first would land on the tie and go to even instead
+    assert oracle.bf16_round((1 + 2.0 ** -8) * (1 + 2.0 ** -30)) == 0x3F81
+    assert oracle.bf16_round((1 + 2.0 ** -8) * (1 - 2.0 ** -30)) == 0x3F80
+    assert oracle.bf16_round(-(1 + 3 * 2.0 ** -8) * (1 - 2.0 ** -30)) == 0xBF81
+    # bf16 subnormals are multiples of 2^-133; the largest rounds up into the normals
+    assert oracle.bf16_round(2.0 ** -133) == 0x0001
+    assert oracle.bf16_round(3 * 2.0 ** -134) == 0x0002       # 1.5 quanta: tie to even
+    assert oracle.bf16_round(2.0 ** -126 - 2.0 ** -140) == 0x0080
+    assert oracle.bf16_round(1e300) == 0x7F80
+
+
+def test_swiglu_backward_closed_forms():
+    rng = np.random.default_rng(32)
+    up = rng.standard_normal(500)
+    dh = rng.standard_normal(500)
+    dg, du, h = oracle.swiglu_backward(np.zeros(500), up, dh)
+    assert np.array_equal(dg, dh * up * 0.5) and np.all(du == 0) and np.all(h == 0)
+    dg, du, h = oracle.swiglu_backward(np.full(500, 64.0), up, dh)
+    assert np.array_equal(dg, dh * up) and np.array_equal(du, 64.0 * dh) and np.array_equal(h, 64.0 * up)
+    ln3 = math.log(3.0)
+    dg, du, h = oracle.swiglu_backward(np.full(500, ln3), up, dh)
+    for i in range(0, 500, 37):
+        assert _ulps(dg[i], dh[i] * up[i] * 0.75 * (1 + 0.25 * ln3)) <= 16
+        assert _ulps(du[i], dh[i] * 0.75 * ln3) <= 8
+        assert _ulps(h[i], 0.75 * ln3 * up[i]) <= 8

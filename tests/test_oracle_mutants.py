@@ -32,11 +32,18 @@ MUTANTS = {
     "wgrad_skip_first": ("for (int64_t t = P[g]; t < P[g + 1]; ++t)", "for (int64_t t = P[g] + 1; t < P[g + 1]; ++t)"),
     "e4m3_bias": ("else v = ldexp((double)(8 + fr), ef - 7 - 3);", "else v = ldexp((double)(8 + fr), ef - 8 - 3);"),
     "silu_sign": ("return x / (1.0 + exp(-x));", "return x / (1.0 + exp(x));"),
-    "swiglu_roles": ("h[i] = mxref_silu(gate[i]) * up[i];", "h[i] = mxref_silu(up[i]) * gate[i];"),
+    "swiglu_roles": ("for (int64_t i = 0; i < M * I; ++i) h[i] = mxref_silu(gate[i]) * up[i];",
+                     "for (int64_t i = 0; i < M * I; ++i) h[i] = mxref_silu(up[i]) * gate[i];"),
+    "bwd_h_roles": ("        h[i] = mxref_silu(gate[i]) * up[i];", "        h[i] = mxref_silu(up[i]) * gate[i];"),
     "f64_signed_amax": ("if (fabs(x[i]) > amax) amax = fabs(x[i]);", "if (x[i] > amax) amax = x[i];"),
     "f64_scale_direction": ("q[i] = mxref_e4m3_encode(ldexp(x[i], 127 - (int)S));",
                             "q[i] = mxref_e4m3_encode(ldexp(x[i], (int)S - 127));"),
     "f64_block_stride": ("const double* blk = x + m * K + b * 32;", "const double* blk = x + m * K + b * 31;"),
+    "dsilu_missing_term": ("return sig * (1.0 + x * (1.0 - sig));", "return sig * (1.0 + x * sig);"),
+    "bwd_dup_uses_dsilu": ("dup[i] = dh[i] * mxref_silu(gate[i]);", "dup[i] = dh[i] * mxref_dsilu(gate[i]);"),
+    "bwd_dgate_no_up": ("dgate[i] = dh[i] * up[i] * mxref_dsilu(gate[i]);", "dgate[i] = dh[i] * mxref_dsilu(gate[i]);"),
+    "bf16_round_truncates": ("double n = nearbyint(ldexp(a, 7 - E));", "double n = floor(ldexp(a, 7 - E));"),
+    "bf16_subnormal_quantum": ("int n = (int)nearbyint(ldexp(a, 133));", "int n = (int)nearbyint(ldexp(a, 134));"),
 }
 
 
