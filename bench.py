@@ -21,6 +21,12 @@ the same with the quantizing SwiGLU epilogue (MXFP8 [32768, 2048] out), the
 ragged 128-expert case next to the dense GEMM of the same size, and the down
 projection forward / dgrad / wgrad.
 
+``moe_layer`` runs one MoE layer's expert computation forward + backward on
+that routing (quantize, gate+up GEMM with the quantizing SwiGLU epilogue, down
+GEMM; then dgrad, wgrad, SwiGLU backward and their quantizations; weights
+re-quantized each step) and reports each stage's time and the quantize /
+GEMM time ratio.
+
 ``roofline`` describes the dominant kernel of the step (its own launch time
 from HIP events on the launch stream); ``cpu_baseline`` times the CPU oracle
 on a bounded sample of the same workload (a reported baseline, not a target).
@@ -277,6 +283,65 @@ def bench_gemm(torch, mx, W, args):
     return out
 
 
+def bench_layer(torch, mx, W, args):
+    """One MoE layer's expert computation, forward + backward, on the gate+up /
+    down workloads' routing (32768 rows, H 7168, I 2048, 16 experts): per-stage
+    GPU time from events recorded between the calls, averaged over the timed
+    steps, plus the step total timed without them."""
+    from mxfp8_block_scaled_04_amd.moe_layer import KIND, MoELayer
+
+    d1 = W.moe_gate_up(seed=args.seed, device="cuda")
+    d2 = W.moe_down_backward(seed=args.seed, device="cuda")
+    assert (d1["offsets"] == d2["offsets"]).all()
+    M, H, I = d1["M"], d1["K"], d1["N"] // 2
+    X, dY = d1["x"], d2["dy"]
+    W1 = mx.swiglu_interleave(d1["w"])
+    W2 = d2["w"]
+    off = torch.from_numpy(d1["offsets"]).to("cuda")
+    del d1, d2
+    torch.cuda.empty_cache()
+    layer = MoELayer(off, M, H, I)
+    step = lambda mark=None: layer.step(X, dY, W1, W2, mark)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    names, events = [], []
+
+    def mark(name):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record()
+        names.append(name)
+        events.append(ev)
+
+    stage = {}
+    for _ in range(args.steps):
+        names.clear()
+        events.clear()
+        mark("start")
+        step(mark)
+        events[-1].synchronize()
+        for i in range(1, len(events)):
+            stage[names[i]] = stage.get(names[i], 0.0) + events[i - 1].elapsed_time(events[i]) / args.steps
+    tm = Timer(torch)
+    ms_step = tm.run(step, args.steps)
+    kinds = {}
+    for n, ms in stage.items():
+        kinds[KIND[n]] = kinds.get(KIND[n], 0.0) + ms
+    quant_act = sum(ms for n, ms in stage.items() if KIND[n] == "quant" and not n.startswith("W"))
+    out = {
+        "workload": f"MoE layer fwd+bwd, M {M}, H {H}, I {I}, {layer.G} experts (Dirichlet(0.5) routing)",
+        "ms_step": ms_step, "tflops": layer.flops() / (ms_step * 1e-3) / 1e12,
+        "ms_by_kind": kinds, "ms_by_stage": stage,
+        "quant_activations_ms": quant_act,
+        "quant_activations_over_gemm": quant_act / kinds["gemm"],
+        "quant_all_over_gemm": kinds["quant"] / kinds["gemm"],
+    }
+    del layer, X, dY, W1, W2
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -284,6 +349,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-gemm", action="store_true", help="skip the grouped-GEMM section")
+    ap.add_argument("--no-layer", action="store_true", help="skip the MoE-layer chain")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=32768, help="rows of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -311,6 +377,7 @@ def main():
         torch.cuda.empty_cache()
     quant, sample = bench_quant(torch, mx, W, args)
     gemm = None if args.no_gemm else bench_gemm(torch, mx, W, args)
+    layer = None if args.no_layer else bench_layer(torch, mx, W, args)
     cpu = None if sample is None else cpu_baseline(sample, args.seed)
 
     ms_step = quant["ms_rows"] + quant["ms_cols"]
@@ -344,6 +411,7 @@ def main():
         "cpu_baseline": cpu,
         "quantize_dual": dict(quant["dual"], workload="bf16 [131072, 7168] -> row-wise + column-wise MXFP8, one read"),
         "gemm": gemm,
+        "moe_layer": layer,
     }
     print(json.dumps(line), flush=True)
 

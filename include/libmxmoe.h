@@ -169,6 +169,10 @@ mx_status mx_grouped_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* W
  *           packed scales ([G*2I][K])
  *   hq      uint8 [M][I] codes; hs packed scales (R = M, contraction I),
  *           ready as the X operand of the down projection
+ *   preact  NULL, or bf16 [M][2I]: also store the gate and up values
+ *           themselves (bf16 of the fp32 accumulators, columns in the
+ *           interleaved order of Wq's rows), as the backward pass of SwiGLU
+ *           needs them; 16-byte aligned
  * Rows of a group are written once; rows outside every group, and the
  * scale bytes of the padding rows [M, 32 ceil(M / 32)), are left untouched
  * (no output row reads them).  Requires K % 256 == 0 and I % 128 == 0
@@ -177,7 +181,7 @@ mx_status mx_grouped_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* W
 mx_status mx_grouped_gemm_swiglu(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq,
                                  const uint8_t* Ws, const int32_t* group_offsets, int32_t G,
                                  int64_t M, int64_t I, int64_t K, uint8_t* hq, uint8_t* hs,
-                                 void* stream);
+                                 uint16_t* preact, void* stream);
 
 /*
  * Data-gradient grouped GEMM (M-grouped, weights read transposed; the
@@ -213,6 +217,27 @@ mx_status mx_grouped_gemm_dgrad(const uint8_t* dYq, const uint8_t* dYs, const ui
 mx_status mx_grouped_gemm_wgrad(const uint8_t* A, const uint8_t* As, const uint8_t* B,
                                 const uint8_t* Bs, const int32_t* padded_offsets, int32_t G,
                                 int64_t N, int64_t K, int64_t Mcap, uint16_t* dW, void* stream);
+
+/*
+ * Backward pass of SwiGLU, the activation between the two projections of
+ * the MoE layer (kucoin.com MoK page, section 02, on the MXFP8 data path
+ * through the SwiGLU step), elementwise over M rows and I hidden units:
+ *   h  = silu(g) u,  silu(g) = g sigma(g),  sigma(g) = 1 / (1 + e^-g)
+ *   dg = dh u sigma(g) (1 + g (1 - sigma(g))),   du = dh silu(g)
+ * computed in fp32, each result rounded to bf16 (nearest even).
+ *   preact  bf16 [M][2I] gate and up values in the interleaved column order
+ *           of mx_grouped_gemm_swiglu (its preact output): columns
+ *           [64 b, 64 b + 32) gate of hidden units [32 b, 32 b + 32),
+ *           [64 b + 32, 64 b + 64) their up values
+ *   dh      bf16 [M][I] gradient of the activation
+ *   dpre    bf16 [M][2I] out: dg and du in the same interleaved order (the
+ *           gradient of the gate+up projection's output)
+ *   h       NULL, or bf16 [M][I] out: the activation itself (for the weight
+ *           gradient of the down projection)
+ * Requires I % 32 == 0 (MX_ERR_SHAPE), 16-byte aligned pointers.
+ */
+mx_status mx_swiglu_backward(const uint16_t* preact, const uint16_t* dh, int64_t M, int64_t I,
+                             uint16_t* dpre, uint16_t* h, void* stream);
 
 #ifdef __cplusplus
 }

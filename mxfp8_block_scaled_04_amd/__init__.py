@@ -49,8 +49,10 @@ def load():
     lib.mx_quantize_dual.restype = ST
     lib.mx_grouped_gemm.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, P]
     lib.mx_grouped_gemm.restype = ST
-    lib.mx_grouped_gemm_swiglu.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, P, P]
+    lib.mx_grouped_gemm_swiglu.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, P, P, P]
     lib.mx_grouped_gemm_swiglu.restype = ST
+    lib.mx_swiglu_backward.argtypes = [P, P, I64, I64, P, P, P]
+    lib.mx_swiglu_backward.restype = ST
     lib.mx_grouped_gemm_dgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, I64, P, P]
     lib.mx_grouped_gemm_dgrad.restype = ST
     lib.mx_grouped_gemm_wgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, P]
@@ -63,6 +65,7 @@ def load():
 SYMBOLS = (
     "mx_status_str", "mx_version", "mx_scale_bytes", "mx_cols_capacity", "mx_quantize_rows",
     "mx_quantize_cols", "mx_quantize_dual", "mx_grouped_gemm", "mx_grouped_gemm_swiglu", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad",
+    "mx_swiglu_backward",
 )
 
 
@@ -188,9 +191,11 @@ def swiglu_interleave(w):
     return torch.stack([gate, up], dim=2).reshape(G, N2, K)
 
 
-def mx_grouped_gemm_swiglu(Xq, Xs, Wq, Ws, group_offsets, hq=None, hs=None, stream=None):
+def mx_grouped_gemm_swiglu(Xq, Xs, Wq, Ws, group_offsets, hq=None, hs=None, preact=None, stream=None):
     """Gate+up grouped GEMM + SwiGLU + MXFP8 quantization of the result.
-    Wq uint8 [G, 2I, K] in swiglu_interleave order; returns (hq uint8 [M, I], hs packed)."""
+    Wq uint8 [G, 2I, K] in swiglu_interleave order.  preact: None, True (allocate)
+    or a bf16 [M, 2I] tensor that also receives the gate/up values.
+    Returns (hq uint8 [M, I], hs packed, preact or None)."""
     M, K = Xq.shape
     G, N2, K2 = Wq.shape
     if K2 != K or N2 % 2:
@@ -200,10 +205,35 @@ def mx_grouped_gemm_swiglu(Xq, Xs, Wq, Ws, group_offsets, hq=None, hs=None, stre
         hq = torch.empty((M, I), dtype=torch.uint8, device=Xq.device)
     if hs is None:
         hs = torch.empty(mx_scale_bytes(M, I), dtype=torch.uint8, device=Xq.device)
+    if preact is True:
+        preact = torch.empty((M, N2), dtype=torch.bfloat16, device=Xq.device)
+    if preact is not None and tuple(preact.shape) != (M, N2):
+        raise ValueError("preact shape")
     rc = load().mx_grouped_gemm_swiglu(_ptr(Xq), _ptr(Xs), _ptr(Wq), _ptr(Ws), _ptr(group_offsets), G, M, I, K,
-                                       _ptr(hq), _ptr(hs), _stream(stream))
+                                       _ptr(hq), _ptr(hs), _ptr(preact), _stream(stream))
     _check(rc, "mx_grouped_gemm_swiglu")
-    return hq, hs
+    return hq, hs, preact
+
+
+def mx_swiglu_backward(preact, dh, dpre=None, h=None, stream=None):
+    """SwiGLU backward: preact bf16 [M, 2I] (interleaved gate/up, as saved by
+    mx_grouped_gemm_swiglu), dh bf16 [M, I] -> (dpre bf16 [M, 2I], h or None).
+    h: None, True (allocate) or a bf16 [M, I] tensor to receive silu(g) u."""
+    M, N2 = preact.shape
+    I = N2 // 2
+    if tuple(dh.shape) != (M, I):
+        raise ValueError("shape mismatch")
+    if not (preact.is_contiguous() and dh.is_contiguous()) or (
+            h is not None and h is not True and not h.is_contiguous()):
+        raise ValueError("contiguous tensors required")
+    if dpre is None:
+        dpre = torch.empty((M, N2), dtype=torch.bfloat16, device=preact.device)
+    if h is True:
+        h = torch.empty((M, I), dtype=torch.bfloat16, device=preact.device)
+    rc = load().mx_swiglu_backward(_ptr(_bits16(preact)), _ptr(_bits16(dh)), M, I, _ptr(dpre), _ptr(h),
+                                   _stream(stream))
+    _check(rc, "mx_swiglu_backward")
+    return dpre, h
 
 
 def mx_grouped_gemm_dgrad(dYq, dYs, WTq, WTs, group_offsets, G, out=None, stream=None):

@@ -118,19 +118,20 @@ mx_status mx_grouped_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* W
 
 mx_status mx_grouped_gemm_swiglu(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
                                  const int32_t* group_offsets, int32_t G, int64_t M, int64_t I, int64_t K,
-                                 uint8_t* hq, uint8_t* hs, void* stream) {
+                                 uint8_t* hq, uint8_t* hs, uint16_t* preact, void* stream) {
     if (M < 0 || I < 0 || K < 0 || K % 32 != 0) return MX_ERR_SHAPE;
     if (G < 1 || G > kMaxGroups) return MX_ERR_SHAPE;
     if (K % 256 != 0 || I % 128 != 0) return MX_ERR_UNSUPPORTED;
     if (M == 0 || I == 0) return MX_OK;
     if (!Xq || !Xs || !Wq || !Ws || !group_offsets || !hq || !hs) return MX_ERR_NULL;
-    if (!aligned16(Xq) || !aligned16(Xs) || !aligned16(Wq) || !aligned16(Ws) || !aligned16(hq) || !aligned16(hs))
+    if (!aligned16(Xq) || !aligned16(Xs) || !aligned16(Wq) || !aligned16(Ws) || !aligned16(hq) || !aligned16(hs) ||
+        (preact && !aligned16(preact)))
         return MX_ERR_ALIGN;
     if (K > (1 << 23) || 2 * I > (1 << 22)) return MX_ERR_UNSUPPORTED;
     if (mx_scale_bytes(M, K) >= ((int64_t)1 << 32) || mx_scale_bytes((int64_t)G * 2 * I, K) >= ((int64_t)1 << 32) ||
         mx_scale_bytes(M, I) >= ((int64_t)1 << 32))
         return MX_ERR_UNSUPPORTED;
-    return from_hip(mx::launch_grouped_gemm_swiglu(Xq, Xs, Wq, Ws, group_offsets, G, M, I, K, hq, hs,
+    return from_hip(mx::launch_grouped_gemm_swiglu(Xq, Xs, Wq, Ws, group_offsets, G, M, I, K, hq, hs, preact,
                                                    (hipStream_t)stream));
 }
 
@@ -169,6 +170,15 @@ mx_status mx_grouped_gemm_wgrad(const uint8_t* A, const uint8_t* As, const uint8
         return MX_ERR_UNSUPPORTED;
     return from_hip(mx::launch_grouped_gemm_wgrad(A, As, B, Bs, padded_offsets, G, N, K, Mcap, dW,
                                                   (hipStream_t)stream));
+}
+
+mx_status mx_swiglu_backward(const uint16_t* preact, const uint16_t* dh, int64_t M, int64_t I, uint16_t* dpre,
+                             uint16_t* h, void* stream) {
+    if (M < 0 || I < 0 || I % 32 != 0) return MX_ERR_SHAPE;
+    if (M == 0 || I == 0) return MX_OK;
+    if (!preact || !dh || !dpre) return MX_ERR_NULL;
+    if (!aligned16(preact) || !aligned16(dh) || !aligned16(dpre) || (h && !aligned16(h))) return MX_ERR_ALIGN;
+    return from_hip(mx::launch_swiglu_backward(preact, dh, M, I, dpre, h, (hipStream_t)stream));
 }
 
 }  // extern "C"

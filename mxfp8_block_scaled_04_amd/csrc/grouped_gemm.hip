@@ -438,9 +438,9 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& a, const Layout& L, 
             B0 = a.B + (int64_t)g * a.K;
             Bs0 = a.Bs + ((int64_t)g * a.K / 256) * 256;
         }
-        // the SwiGLU epilogue needs the tile's first row and column tile
-        // apart (no 64-bit division in the kernel): it gets them packed
-        T.outoff = EPI == 1 ? (arow0 << 24) + nt : arow0 * a.N + nt * TN;
+        // the SwiGLU epilogues need the tile's first row and column tile
+        // apart (no 64-bit division in the kernel): they get them packed
+        T.outoff = EPI != 0 ? (arow0 << 24) + nt : arow0 * a.N + nt * TN;
         T.rows = (int32_t)(arows < TM ? arows : TM);
         T.cols = (int32_t)((a.N - nt * TN) < TN ? (a.N - nt * TN) : TN);
     } else {
@@ -493,12 +493,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)y) << 16);
 }
 
+// Row blocks [I0, I1) of the wave's share (all four by default).
+template <int I0 = 0, int I1 = 4>
 __device__ __forceinline__ void epilogue16(uint16_t* out, const Tile& T, const Layout& L, f32x16 (&acc)[4][4], int wm,
                                            int wn, int h, int r32) {
-    const i32x4 ro = make_rsrc(out + T.outoff, (uint32_t)T.rows * L.ldo * 2u);
+    const i32x4 ro = make_rsrc(out, (uint32_t)T.rows * L.ldo * 2u);
     const uint32_t zero = uni(0u);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = I0; i < I1; ++i) {
         const uint32_t rowoff = (uint32_t)(wm * 128 + i * 32 + r32) * L.ldo * 2u;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -548,6 +550,7 @@ __device__ __forceinline__ void bstore1(const i32x4& rs, uint32_t voff, uint32_t
     asm volatile("buffer_store_byte %0, %1, %2, %3 offen" ::"v"(v), "v"(voff), "s"(rs), "s"(soff) : "memory");
 }
 
+template <int I0 = 0, int I1 = 4>
 __device__ __forceinline__ void epilogue_swiglu(const GemmArgs& a, const Tile& T, f32x16 (&acc)[4][4], int wm, int wn,
                                                 int h, int r32) {
     const int64_t I = a.N / 2;
@@ -561,7 +564,7 @@ __device__ __forceinline__ void epilogue_swiglu(const GemmArgs& a, const Tile& T
     const i32x4 rsc = make_rsrc(a.hs, (uint32_t)hs_bytes);
     const uint32_t zero = uni(0u);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = I0; i < I1; ++i) {
         const int row = wm * 128 + i * 32 + r32;
         const int64_t grow = row0 + row;
 #pragma unroll
@@ -627,10 +630,13 @@ __device__ __forceinline__ void epilogue_any(uint16_t* out, int rows, int cols, 
 }
 
 // VEC16: output rows are 16-byte aligned (ldo % 8 == 0): 16-byte epilogue.
-// EPI 1: quantizing SwiGLU epilogue instead of bf16 output (mode 0).
+// EPI 1: quantizing SwiGLU epilogue instead of bf16 output (mode 0);
+// EPI 2: both, the bf16 gate/up tile first (32 + 40 stores per wave, more
+// than the 6-bit store count can name: the next tile waits down to 63, which
+// still covers every load issued before the epilogue).
 template <bool VEC16, int EPI>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs a) {
-    constexpr int kEpiWait = EPI == 1 ? kSwigluStores : (VEC16 ? 32 : 0);
+    constexpr int kEpiWait = EPI == 2 ? 63 : EPI == 1 ? kSwigluStores : (VEC16 ? 32 : 0);
     const int t = threadIdx.x;
     const int w = t >> 6;
     const int l = t & 63;
@@ -784,9 +790,25 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs a) {
             run_chunk<kEpiWait>(P, acc, X, c == 0 && !first && kEpiWait > 0, Ln, L, w, l, wm, wn, la0, la1, lb0,
                                 lb1);
         }
-        if (EPI == 1) epilogue_swiglu(a, T, acc, wm, wn, h, r32);
-        else if (VEC16) epilogue16(a.out, T, L, acc, wm, wn, h, r32);
-        else epilogue_any(a.out + T.outoff, T.rows, T.cols, L.ldo, acc, wm, wn, h, r32);
+        if (EPI == 2) {
+            // bf16 gate/up and the quantized activation, one 32-row block at
+            // a time (fewer values live at once)
+            uint16_t* const pre = a.out + (T.outoff >> 24) * a.N + (T.outoff & 0xFFFFFF) * TN;
+            epilogue16<0, 1>(pre, T, L, acc, wm, wn, h, r32);
+            epilogue_swiglu<0, 1>(a, T, acc, wm, wn, h, r32);
+            epilogue16<1, 2>(pre, T, L, acc, wm, wn, h, r32);
+            epilogue_swiglu<1, 2>(a, T, acc, wm, wn, h, r32);
+            epilogue16<2, 3>(pre, T, L, acc, wm, wn, h, r32);
+            epilogue_swiglu<2, 3>(a, T, acc, wm, wn, h, r32);
+            epilogue16<3, 4>(pre, T, L, acc, wm, wn, h, r32);
+            epilogue_swiglu<3, 4>(a, T, acc, wm, wn, h, r32);
+        } else if (EPI == 1) {
+            epilogue_swiglu(a, T, acc, wm, wn, h, r32);
+        } else if (VEC16) {
+            epilogue16(a.out + T.outoff, T, L, acc, wm, wn, h, r32);
+        } else {
+            epilogue_any(a.out + T.outoff, T.rows, T.cols, L.ldo, acc, wm, wn, h, r32);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -856,7 +878,7 @@ hipError_t launch_grouped_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8
 
 hipError_t launch_grouped_gemm_swiglu(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
                                       const int32_t* group_offsets, int32_t G, int64_t M, int64_t I, int64_t K,
-                                      uint8_t* hq, uint8_t* hs, hipStream_t stream) {
+                                      uint8_t* hq, uint8_t* hs, uint16_t* preact, hipStream_t stream) {
     if (M == 0 || I == 0) return hipSuccess;
     GemmArgs a = {};
     a.A = Xq;
@@ -864,7 +886,7 @@ hipError_t launch_grouped_gemm_swiglu(const uint8_t* Xq, const uint8_t* Xs, cons
     a.B = Wq;
     a.Bs = Ws;
     a.offsets = group_offsets;
-    a.out = nullptr;
+    a.out = preact;
     a.M = M;
     a.N = 2 * I;
     a.K = K;
@@ -879,7 +901,8 @@ hipError_t launch_grouped_gemm_swiglu(const uint8_t* Xq, const uint8_t* Xs, cons
     const int64_t ub = ((M + TM - 1) / TM + G) * ((2 * I + TN - 1) / TN);
     int64_t nwg = num_cus();
     if (ub < nwg) nwg = ub;
-    hipLaunchKernelGGL((grouped_gemm_kernel<true, 1>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
+    if (preact) hipLaunchKernelGGL((grouped_gemm_kernel<true, 2>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((grouped_gemm_kernel<true, 1>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -23,7 +23,7 @@ hipError_t launch_grouped_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8
 
 hipError_t launch_grouped_gemm_swiglu(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq, const uint8_t* Ws,
                                       const int32_t* group_offsets, int32_t G, int64_t M, int64_t I, int64_t K,
-                                      uint8_t* hq, uint8_t* hs, hipStream_t stream);
+                                      uint8_t* hq, uint8_t* hs, uint16_t* preact, hipStream_t stream);
 
 hipError_t launch_grouped_gemm_dgrad(const uint8_t* dYq, const uint8_t* dYs, const uint8_t* WTq,
                                      const uint8_t* WTs, const int32_t* group_offsets, int32_t G, int64_t M,
@@ -33,5 +33,8 @@ hipError_t launch_grouped_gemm_wgrad(const uint8_t* A, const uint8_t* As, const 
                                      const uint8_t* Bs, const int32_t* padded_offsets, int32_t G,
                                      int64_t N, int64_t K, int64_t Mcap, uint16_t* dW,
                                      hipStream_t stream);
+
+hipError_t launch_swiglu_backward(const uint16_t* preact, const uint16_t* dh, int64_t M, int64_t I, uint16_t* dpre,
+                                  uint16_t* h, hipStream_t stream);
 
 }  // namespace mx

@@ -1,0 +1,157 @@
+"""One MoE layer's expert computation on one GPU, forward and backward, as a
+chain of libmxmoe calls (no router and no dispatch/combine: the token rows
+arrive grouped by expert).  This is the layer-level view of the public
+write-ups on Cursor's MXFP8 MoE kernels (aigc.bar "被忽视的量化税": the
+quantization passes next to the grouped GEMMs of a layer; lpnh.cn 2479732
+section 1: the forward and backward passes and the transposed quantization
+the backward needs; kucoin.com MoK page, section 02: MXFP8 built into the
+grouped-GEMM and SwiGLU data path).
+
+Shapes: X [M, H] token rows, group offsets [G+1] (rows of expert g are
+[o_g, o_{g+1})); W1 [G, 2I, H] gate+up weights in the interleaved row order
+of ``swiglu_interleave``; W2 [G, H, I] down weights.
+
+  forward    F1  X -> row-wise Xq (gate+up operand) and column-wise X^T
+                 (gate+up weight gradient)            mx_quantize_dual
+             F2  hq = MXFP8(silu(X W1g^T) * X W1u^T), and the bf16 gate/up
+                 values for the backward pass         mx_grouped_gemm_swiglu
+             F3  Y = hq W2^T                          mx_grouped_gemm
+  backward   B1  dY -> row-wise (down dgrad) and column-wise (down wgrad)
+                                                      mx_quantize_dual
+             B2  dH = dY W2                           mx_grouped_gemm_dgrad
+             B3  d(gate, up) and h from dH and the saved gate/up
+                                                      mx_swiglu_backward
+             B4  h -> column-wise h^T                 mx_quantize_cols
+             B5  dW2 = dY^T h per expert              mx_grouped_gemm_wgrad
+             B6  d(gate, up) -> row-wise and column-wise
+                                                      mx_quantize_dual
+             B7  dX = d(gate, up) W1                  mx_grouped_gemm_dgrad
+             B8  dW1 = d(gate, up)^T X per expert     mx_grouped_gemm_wgrad
+  weights    W1, W2 -> row-wise (forward operands) and column-wise (dgrad
+             operands, one group per expert)          mx_quantize_dual
+
+Every step runs in the library's kernels; this module only allocates the
+buffers once and issues the calls in order on the current stream.
+"""
+import torch
+
+from . import (mx_cols_capacity, mx_grouped_gemm, mx_grouped_gemm_dgrad, mx_grouped_gemm_swiglu,
+               mx_grouped_gemm_wgrad, mx_quantize_cols, mx_quantize_dual, mx_scale_bytes, mx_swiglu_backward)
+
+FORWARD = ("F1 quantize X", "F2 gate+up GEMM + SwiGLU + quantize", "F3 down GEMM")
+BACKWARD = ("B1 quantize dY", "B2 down dgrad", "B3 SwiGLU backward", "B4 quantize h (cols)", "B5 down wgrad",
+            "B6 quantize d(gate,up)", "B7 gate+up dgrad", "B8 gate+up wgrad")
+WEIGHTS = ("W1 quantize", "W2 quantize")
+KIND = {
+    "F1 quantize X": "quant", "F2 gate+up GEMM + SwiGLU + quantize": "gemm", "F3 down GEMM": "gemm",
+    "B1 quantize dY": "quant", "B2 down dgrad": "gemm", "B3 SwiGLU backward": "elementwise",
+    "B4 quantize h (cols)": "quant", "B5 down wgrad": "gemm", "B6 quantize d(gate,up)": "quant",
+    "B7 gate+up dgrad": "gemm", "B8 gate+up wgrad": "gemm", "W1 quantize": "quant", "W2 quantize": "quant",
+}
+
+
+def _u8(*shape, device):
+    return torch.empty(shape, dtype=torch.uint8, device=device)
+
+
+def _bf16(*shape, device):
+    return torch.empty(shape, dtype=torch.bfloat16, device=device)
+
+
+class QuantPair:
+    """Row-wise and column-wise MXFP8 buffers of a bf16 [R, C] tensor whose
+    rows form G groups."""
+
+    def __init__(self, R, C, G, device):
+        self.Mcap = mx_cols_capacity(R, G)
+        self.q = _u8(R, C, device=device)
+        self.s = _u8(mx_scale_bytes(R, C), device=device)
+        self.qT = _u8(C, self.Mcap, device=device)
+        self.sT = _u8(mx_scale_bytes(C, self.Mcap), device=device)
+        self.P = torch.empty(G + 1, dtype=torch.int32, device=device)
+
+    def fill(self, x, offsets):
+        mx_quantize_dual(x, offsets, self.Mcap, self.q, self.s, self.qT, self.sT, self.P)
+
+
+class MoELayer:
+    """Buffers and calls of one layer for fixed M, H, I and routing."""
+
+    def __init__(self, offsets, M, H, I, device="cuda"):
+        self.M, self.H, self.I = M, H, I
+        self.offsets = offsets
+        G = self.G = offsets.numel() - 1
+        self.woff1 = torch.arange(G + 1, dtype=torch.int32, device=device) * (2 * I)
+        self.woff2 = torch.arange(G + 1, dtype=torch.int32, device=device) * H
+        self.w1 = QuantPair(G * 2 * I, H, G, device)
+        self.w2 = QuantPair(G * H, I, G, device)
+        self.x = QuantPair(M, H, G, device)
+        self.hq = _u8(M, I, device=device)
+        self.hs = _u8(mx_scale_bytes(M, I), device=device)
+        self.preact = _bf16(M, 2 * I, device=device)
+        self.y = _bf16(M, H, device=device)
+        self.dy = QuantPair(M, H, G, device)
+        self.dh = _bf16(M, I, device=device)
+        self.dpre = _bf16(M, 2 * I, device=device)
+        self.h = _bf16(M, I, device=device)
+        self.hT = _u8(I, self.x.Mcap, device=device)
+        self.hTs = _u8(mx_scale_bytes(I, self.x.Mcap), device=device)
+        self.hP = torch.empty(G + 1, dtype=torch.int32, device=device)
+        self.dW2 = _bf16(G, H, I, device=device)
+        self.dgu = QuantPair(M, 2 * I, G, device)
+        self.dx = _bf16(M, H, device=device)
+        self.dW1 = _bf16(G, 2 * I, H, device=device)
+
+    def flops(self):
+        """Matrix flops of one forward + backward over the routed rows."""
+        fwd = 2 * self.M * (2 * self.I) * self.H + 2 * self.M * self.H * self.I
+        return 3 * fwd
+
+    # -- the steps; mark(name) is called after each one is issued --
+    def quantize_weights(self, W1, W2, mark=None):
+        G = self.G
+        self.w1.fill(W1.reshape(G * 2 * self.I, self.H), self.woff1)
+        _mark(mark, "W1 quantize")
+        self.w2.fill(W2.reshape(G * self.H, self.I), self.woff2)
+        _mark(mark, "W2 quantize")
+
+    def forward(self, X, mark=None):
+        G, H, I = self.G, self.H, self.I
+        self.x.fill(X, self.offsets)
+        _mark(mark, FORWARD[0])
+        mx_grouped_gemm_swiglu(self.x.q, self.x.s, self.w1.q.view(G, 2 * I, H), self.w1.s, self.offsets,
+                               hq=self.hq, hs=self.hs, preact=self.preact)
+        _mark(mark, FORWARD[1])
+        mx_grouped_gemm(self.hq, self.hs, self.w2.q.view(G, H, I), self.w2.s, self.offsets, out=self.y)
+        _mark(mark, FORWARD[2])
+        return self.y
+
+    def backward(self, dY, mark=None):
+        G = self.G
+        self.dy.fill(dY, self.offsets)
+        _mark(mark, BACKWARD[0])
+        mx_grouped_gemm_dgrad(self.dy.q, self.dy.s, self.w2.qT, self.w2.sT, self.offsets, G, out=self.dh)
+        _mark(mark, BACKWARD[1])
+        mx_swiglu_backward(self.preact, self.dh, dpre=self.dpre, h=self.h)
+        _mark(mark, BACKWARD[2])
+        mx_quantize_cols(self.h, self.offsets, self.x.Mcap, self.hT, self.hTs, self.hP)
+        _mark(mark, BACKWARD[3])
+        mx_grouped_gemm_wgrad(self.dy.qT, self.dy.sT, self.hT, self.hTs, self.dy.P, dW=self.dW2)
+        _mark(mark, BACKWARD[4])
+        self.dgu.fill(self.dpre, self.offsets)
+        _mark(mark, BACKWARD[5])
+        mx_grouped_gemm_dgrad(self.dgu.q, self.dgu.s, self.w1.qT, self.w1.sT, self.offsets, G, out=self.dx)
+        _mark(mark, BACKWARD[6])
+        mx_grouped_gemm_wgrad(self.dgu.qT, self.dgu.sT, self.x.qT, self.x.sT, self.x.P, dW=self.dW1)
+        _mark(mark, BACKWARD[7])
+        return self.dx, self.dW1, self.dW2
+
+    def step(self, X, dY, W1, W2, mark=None):
+        self.quantize_weights(W1, W2, mark)
+        self.forward(X, mark)
+        return self.backward(dY, mark)
+
+
+def _mark(mark, name):
+    if mark is not None:
+        mark(name)

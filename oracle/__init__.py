@@ -106,6 +106,7 @@ def _load():
     lib.mxref_dsilu.restype = ctypes.c_double
     lib.mxref_bf16_round.argtypes = [ctypes.c_double]
     lib.mxref_bf16_round.restype = ctypes.c_uint16
+    lib.mxref_bf16_round_n.argtypes = [P, I64, P]
     lib.mxref_swiglu_backward.argtypes = [P, P, P, I64, P, P, P]
     _lib = lib
     return lib
@@ -335,9 +336,10 @@ def dsilu(x):
 
 def bf16_round(x):
     """double array -> bf16 bit patterns (uint16), nearest even, one rounding."""
-    a = np.asarray(x, np.float64)
-    f = _load().mxref_bf16_round
-    return np.array([f(float(v)) for v in a.reshape(-1)], np.uint16).reshape(a.shape)
+    a, p = _c(x, np.float64)
+    out = np.empty(a.shape, np.uint16)
+    _load().mxref_bf16_round_n(p, a.size, out.ctypes.data_as(ctypes.c_void_p))
+    return out
 
 
 def swiglu_backward(gate, up, dh):

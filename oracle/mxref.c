@@ -361,6 +361,10 @@ uint16_t mxref_bf16_round(double x) {
     return (uint16_t)(sign | ((E + 127) << 7) | ((int)n - 128));
 }
 
+void mxref_bf16_round_n(const double* x, int64_t n, uint16_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = mxref_bf16_round(x[i]);
+}
+
 void mxref_swiglu_backward(const double* gate, const double* up, const double* dh, int64_t n, double* dgate,
                            double* dup, double* h) {
     for (int64_t i = 0; i < n; ++i) {

@@ -110,6 +110,7 @@ void mxref_swiglu_quantize(const double* gate, const double* up, int64_t M, int6
 /* SwiGLU backward (readings in mxref.c); all arrays of n doubles. */
 double mxref_dsilu(double x);
 uint16_t mxref_bf16_round(double x);
+void mxref_bf16_round_n(const double* x, int64_t n, uint16_t* out);
 void mxref_swiglu_backward(const double* gate, const double* up, const double* dh, int64_t n, double* dgate,
                            double* dup, double* h);
 

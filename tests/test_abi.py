@@ -103,17 +103,30 @@ def test_grouped_gemm_validation():
 
 def test_grouped_gemm_swiglu_validation():
     f = mx.load().mx_grouped_gemm_swiglu
-    # (Xq, Xs, Wq, Ws, offsets, G, M, I, K, hq, hs, stream)
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 2048, 288, FAKE, FAKE, None) == 5   # K % 256 != 0
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 192, 512, FAKE, FAKE, None) == 5   # I % 128 != 0
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 2048, 250, FAKE, FAKE, None) == 2  # K % 32 != 0
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 512, 2048, 512, FAKE, FAKE, None) == 2  # G < 1
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, -1, 2048, 512, FAKE, FAKE, None) == 2   # M < 0
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 2048, 512, None, FAKE, None) == 1  # NULL hq
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 2048, 512, FAKE, None, None) == 1  # NULL hs
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 2048, 512, FAKE, P(0x100001), None) == 3  # misaligned hs
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 1 << 22, 512, FAKE, FAKE, None) == 5  # 2I past the limit
-    assert f(None, None, None, None, None, 4, 0, 2048, 512, None, None, None) == 0    # M == 0: no work
+    # (Xq, Xs, Wq, Ws, offsets, G, M, I, K, hq, hs, preact, stream)
+    F5 = (FAKE,) * 5
+    assert f(*F5, 4, 512, 2048, 288, FAKE, FAKE, None, None) == 5        # K % 256 != 0
+    assert f(*F5, 4, 512, 192, 512, FAKE, FAKE, None, None) == 5         # I % 128 != 0
+    assert f(*F5, 4, 512, 2048, 250, FAKE, FAKE, None, None) == 2        # K % 32 != 0
+    assert f(*F5, 0, 512, 2048, 512, FAKE, FAKE, None, None) == 2        # G < 1
+    assert f(*F5, 4, -1, 2048, 512, FAKE, FAKE, None, None) == 2         # M < 0
+    assert f(*F5, 4, 512, 2048, 512, None, FAKE, None, None) == 1        # NULL hq
+    assert f(*F5, 4, 512, 2048, 512, FAKE, None, None, None) == 1        # NULL hs
+    assert f(*F5, 4, 512, 2048, 512, FAKE, P(0x100001), None, None) == 3  # misaligned hs
+    assert f(*F5, 4, 512, 2048, 512, FAKE, FAKE, P(0x100002), None) == 3  # misaligned preact
+    assert f(*F5, 4, 512, 1 << 22, 512, FAKE, FAKE, None, None) == 5     # 2I past the limit
+    assert f(None, None, None, None, None, 4, 0, 2048, 512, None, None, None, None) == 0  # M == 0: no work
+
+
+def test_swiglu_backward_validation():
+    f = mx.load().mx_swiglu_backward
+    # (preact, dh, M, I, dpre, h, stream)
+    assert f(FAKE, FAKE, 64, 48, FAKE, FAKE, None) == 2            # I % 32 != 0
+    assert f(FAKE, FAKE, -1, 64, FAKE, FAKE, None) == 2            # M < 0
+    assert f(None, FAKE, 64, 64, FAKE, FAKE, None) == 1            # NULL preact
+    assert f(FAKE, FAKE, 64, 64, None, FAKE, None) == 1            # NULL dpre
+    assert f(FAKE, FAKE, 64, 64, FAKE, P(0x100008), None) == 3     # misaligned h
+    assert f(None, None, 0, 64, None, None, None) == 0             # M == 0: no work
 
 
 def test_dgrad_validation():

@@ -1,0 +1,124 @@
+"""The MoE-layer chain (mxfp8_block_scaled_04_amd.moe_layer) on a small layer:
+each stage's output against the fp64 oracle computed from that stage's own
+GPU inputs, so a wrong buffer or operand anywhere in the chain shows up at
+its stage.  The kernels themselves have their own parity tests; tolerances
+here are theirs (GEMMs: 8e-3 |ref| + 1e-3 rms; quantization: bit-exact)."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_block_scaled_04_amd as mx
+import oracle
+from mxfp8_block_scaled_04_amd import workloads as W
+from mxfp8_block_scaled_04_amd.moe_layer import BACKWARD, FORWARD, WEIGHTS, MoELayer
+from tests.mxtest import bf16_to_f64, bits, canonical_scales, gemm_tolerance_ok, u8
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    mx.load()
+
+
+def wT_operands(qT, sT, G, Nout, Kin):
+    """Expert g's W^T [Kin, Nout] from a column-wise quantized [G*Nout, Kin]
+    weight (columns [g Nout, (g+1) Nout)) as oracle GEMM operands."""
+    Wcap = qT.shape[1]
+    q = u8(qT)
+    s = canonical_scales(sT, Kin, Wcap)
+    Bq = np.stack([q[:, g * Nout:(g + 1) * Nout] for g in range(G)])
+    Bs = np.stack([s[:, g * Nout // 32:(g + 1) * Nout // 32] for g in range(G)])
+    return Bq, Bs
+
+
+def check_points(got, ref):
+    ok, ratio = gemm_tolerance_ok(got, ref)
+    assert ok, ratio
+
+
+def test_moe_layer_chain_stages():
+    sizes = [300, 0, 150, 250]
+    G, H, I = len(sizes), 512, 256
+    M = sum(sizes)
+    off_h = W.offsets_from_sizes(sizes)
+    off = torch.from_numpy(off_h).to(DEV)
+    X = W.normal_bf16((M, H), 1.0, 1, DEV)
+    W1 = mx.swiglu_interleave(W.normal_bf16((G, 2 * I, H), 1.2 / np.sqrt(H), 2, DEV))
+    W2 = W.normal_bf16((G, H, I), 0.05, 3, DEV)
+    dY = W.normal_bf16((M, H), 1.0, 4, DEV)
+    layer = MoELayer(off, M, H, I)
+    seen = []
+    layer.step(X, dY, W1, W2, mark=seen.append)
+    torch.cuda.synchronize()
+    assert seen == list(WEIGHTS + FORWARD + BACKWARD)
+    rng = np.random.default_rng(0)
+
+    # weights and F1: bit-exact quantizations
+    q, s = oracle.quantize_rows(bits(W1.reshape(G * 2 * I, H)))
+    assert np.array_equal(u8(layer.w1.q), q) and np.array_equal(canonical_scales(layer.w1.s, G * 2 * I, H), s)
+    qT, sT, P = oracle.quantize_cols(bits(W2.reshape(G * H, I)), (np.arange(G + 1) * H).astype(np.int32),
+                                     layer.w2.Mcap)
+    assert np.array_equal(u8(layer.w2.qT), qT)
+    q, s = oracle.quantize_rows(bits(X))
+    assert np.array_equal(u8(layer.x.q), q)
+    qT, sT, P = oracle.quantize_cols(bits(X), off_h, layer.x.Mcap)
+    assert np.array_equal(u8(layer.x.qT), qT) and np.array_equal(layer.x.P.cpu().numpy(), P)
+
+    # F2: the fused kernel on the chain's operands, called on its own
+    hq, hs, pre = mx.mx_grouped_gemm_swiglu(layer.x.q, layer.x.s, layer.w1.q.view(G, 2 * I, H), layer.w1.s, off,
+                                            preact=True)
+    torch.cuda.synchronize()
+    assert torch.equal(hq, layer.hq)
+    assert np.array_equal(canonical_scales(hs, M, I), canonical_scales(layer.hs, M, I))
+    assert torch.equal(pre.view(torch.int16), layer.preact.view(torch.int16))
+
+    # F3: Y = hq W2^T
+    rows = rng.integers(0, M, 1500)
+    cols = rng.integers(0, H, 1500)
+    W2q = u8(layer.w2.q).reshape(G, H, I)
+    W2s = canonical_scales(layer.w2.s, G * H, I).reshape(G, H, I // 32)
+    ref = oracle.grouped_gemm_points(u8(layer.hq), canonical_scales(layer.hs, M, I), W2q, W2s, off_h, rows, cols)
+    check_points(bf16_to_f64(layer.y)[rows, cols], ref)
+
+    # B1 + B2: dH = dY W2
+    q, s = oracle.quantize_rows(bits(dY))
+    assert np.array_equal(u8(layer.dy.q), q)
+    Bq, Bs = wT_operands(layer.w2.qT, layer.w2.sT, G, H, I)
+    cols = rng.integers(0, I, 1500)
+    ref = oracle.grouped_gemm_points(q, s, Bq, Bs, off_h, rows, cols)
+    check_points(bf16_to_f64(layer.dh)[rows, cols], ref)
+
+    # B3: SwiGLU backward on the saved gate/up and dH
+    dpre, h = mx.mx_swiglu_backward(layer.preact, layer.dh, h=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dpre.view(torch.int16), layer.dpre.view(torch.int16))
+    assert torch.equal(h.view(torch.int16), layer.h.view(torch.int16))
+
+    # B4 + B5: dW2 = dY^T h per expert
+    qT, sT, P = oracle.quantize_cols(bits(layer.h), off_h, layer.x.Mcap)
+    assert np.array_equal(u8(layer.hT), qT)
+    Aq, As = u8(layer.dy.qT), canonical_scales(layer.dy.sT, H, layer.x.Mcap)
+    gs = rng.integers(0, G, 1500)
+    ns = rng.integers(0, H, 1500)
+    ks = rng.integers(0, I, 1500)
+    ref = oracle.wgrad_points(Aq, As, qT, sT, P, gs, ns, ks)
+    check_points(bf16_to_f64(layer.dW2)[gs, ns, ks], ref)
+
+    # B6 + B7: dX = d(gate, up) W1
+    q, s = oracle.quantize_rows(bits(layer.dpre))
+    assert np.array_equal(u8(layer.dgu.q), q)
+    Bq, Bs = wT_operands(layer.w1.qT, layer.w1.sT, G, 2 * I, H)
+    cols = rng.integers(0, H, 1500)
+    ref = oracle.grouped_gemm_points(q, s, Bq, Bs, off_h, rows, cols)
+    check_points(bf16_to_f64(layer.dx)[rows, cols], ref)
+
+    # B8: dW1 = d(gate, up)^T X per expert
+    qT, sT, P = oracle.quantize_cols(bits(layer.dpre), off_h, layer.x.Mcap)
+    assert np.array_equal(u8(layer.dgu.qT), qT)
+    ns = rng.integers(0, 2 * I, 1500)
+    ks = rng.integers(0, H, 1500)
+    ref = oracle.wgrad_points(qT, sT, u8(layer.x.qT), canonical_scales(layer.x.sT, H, layer.x.Mcap), P, gs, ns, ks)
+    check_points(bf16_to_f64(layer.dW1)[gs, ns, ks], ref)

@@ -31,7 +31,7 @@ import torch
 import mxfp8_block_scaled_04_amd as mx
 import oracle
 from mxfp8_block_scaled_04_amd import workloads as W
-from tests.mxtest import canonical_scales, u8
+from tests.mxtest import bf16_to_f64, canonical_scales, gemm_tolerance_ok, u8
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -213,3 +213,32 @@ def test_swiglu_gate_up_sampled():
     s = oracle.unpack_scales(u8(hs), M, I)
     cols = blocks[:, None] * 32 + np.arange(32)[None, :]
     check_blocks(q[rows[:, None], cols], s[rows, blocks], h, gate, up, Ag, Au, K)
+
+
+@pytest.mark.parametrize("sizes,I,K", [([100, 0, 37, 300, 163], 256, 512), ([1, 31, 0, 257], 128, 256)])
+def test_swiglu_preact_output(sizes, I, K):
+    """preact = the bf16 gate/up values: bit-identical to mx_grouped_gemm on the
+    same interleaved weights (same matrix instructions in the same order),
+    within the GEMM tolerance of the oracle; hq and hs unchanged by it."""
+    M, G = sum(sizes), len(sizes)
+    off = W.offsets_from_sizes(sizes)
+    x = W.normal_bf16((M, K), 1.0, 300 + M, DEV)
+    w = W.normal_bf16((G, 2 * I, K), 1.2 / np.sqrt(K), 400 + K, DEV)
+    Xq, Xs = mx.mx_quantize_rows(x)
+    Wq, Ws = mx.mx_quantize_rows(mx.swiglu_interleave(w).reshape(G * 2 * I, K))
+    Wq = Wq.reshape(G, 2 * I, K)
+    off_dev = torch.from_numpy(off).to(DEV)
+    hq0, hs0, none = mx.mx_grouped_gemm_swiglu(Xq, Xs, Wq, Ws, off_dev)
+    assert none is None
+    pre = torch.full((M, 2 * I), 0x7FC0, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    hq1, hs1, pre = mx.mx_grouped_gemm_swiglu(Xq, Xs, Wq, Ws, off_dev, preact=pre)
+    y = mx.mx_grouped_gemm(Xq, Xs, Wq, Ws, off_dev)
+    torch.cuda.synchronize()
+    assert torch.equal(hq0, hq1)
+    # scale bytes of rows [M, 32 ceil(M/32)) are not written: compare real rows
+    assert np.array_equal(canonical_scales(hs0, M, I), canonical_scales(hs1, M, I))
+    assert torch.equal(pre.view(torch.int16), y.view(torch.int16))
+    ref = oracle.grouped_gemm(u8(Xq), canonical_scales(Xs, M, K), u8(Wq),
+                              canonical_scales(Ws, G * 2 * I, K).reshape(G, 2 * I, K // 32), off)
+    ok, ratio = gemm_tolerance_ok(bf16_to_f64(pre), ref)
+    assert ok, ratio
