@@ -237,7 +237,8 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(const uint1
 // 64 columns:
 //  * row-wise: in the load phase, the 4 lanes of a DPP quad hold one
 //    32-column block of each of their two rows; quad max, codes stored 8
-//    bytes per lane straight to the row-major result, scale bytes collected
+//    bytes per lane to the row-major result, those of sub-tiles 2p and
+//    2p + 1 together (128 contiguous bytes per row), scale bytes collected
 //    in LDS in packed dword order (the chunk's 8 blocks of a row are two
 //    dwords) and written once per row at the end, 128 contiguous bytes per
 //    32 rows;
@@ -306,6 +307,9 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(const uint16_t* __re
         }
     };
     load(0);
+    // row-wise codes of an even sub-tile wait in registers and go out next to
+    // the odd sub-tile's, so each row gets 128 contiguous bytes at once
+    uint2 pend[4][2];
     uint8_t* rs = reinterpret_cast<uint8_t*>(row_s);
     uint8_t* us = reinterpret_cast<uint8_t*>(unit_s);
 #pragma unroll 1
@@ -320,9 +324,20 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(const uint16_t* __re
             const int64_t r0 = row_begin + 2 * pr, r1 = r0 + 1;
             const uint32_t Sa = scale_from_maxmag(quad_max_u32(max_mag8(da[i])));
             const uint32_t Sb = scale_from_maxmag(quad_max_u32(max_mag8(db[i])));
-            if (g >= 0 && ncol < N) {
-                if (r0 < row_end) store_stream8(q + r0 * N + ncol, quant8(da[i], Sa));
-                if (r1 < row_end) store_stream8(q + r1 * N + ncol, quant8(db[i], Sb));
+            const uint2 ca = quant8(da[i], Sa), cb = quant8(db[i], Sb);
+            if (st & 1) {
+                const int64_t pcol = ncol - 64;
+                if (g >= 0 && pcol < N) {
+                    if (r0 < row_end) store_stream8(q + r0 * N + pcol, pend[i][0]);
+                    if (r1 < row_end) store_stream8(q + r1 * N + pcol, pend[i][1]);
+                }
+                if (g >= 0 && ncol < N) {
+                    if (r0 < row_end) store_stream8(q + r0 * N + ncol, ca);
+                    if (r1 < row_end) store_stream8(q + r1 * N + ncol, cb);
+                }
+            } else {
+                pend[i][0] = ca;
+                pend[i][1] = cb;
             }
             if ((t & 3) == 0) {
                 rs[(2 * pr) * 8 + (b & 1) * 4 + (b >> 1)] = (uint8_t)Sa;
