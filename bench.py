@@ -283,6 +283,29 @@ def bench_gemm(torch, mx, W, args):
     return out
 
 
+def bench_vendor(torch, W, args):
+    """The vendor library's block-scaled GEMM on the ragged case's dense twin
+    (65536 x 2048 x 7168, E4M3 with E8M0 scales per 32 of K, bf16 out) through
+    torch._scaled_mm, for context.  Operands are seeded random codes with unit
+    scales: the timing does not depend on the values."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(args.seed)
+    M, N, K = 65536, 2048, 7168
+    a = torch.randn((M, K), device="cuda", generator=g).mul_(0.5).to(torch.float8_e4m3fn)
+    b = torch.randn((N, K), device="cuda", generator=g).mul_(0.5).to(torch.float8_e4m3fn)
+    sa = torch.full((M, K // 32), 127, dtype=torch.uint8, device="cuda").view(torch.float8_e8m0fnu)
+    sb = torch.full((N, K // 32), 127, dtype=torch.uint8, device="cuda").view(torch.float8_e8m0fnu)
+    fn = lambda: torch._scaled_mm(a, b.t(), sa, sb, out_dtype=torch.bfloat16)
+    try:
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ms = Timer(torch).run(fn, args.steps)
+    except Exception as ex:  # the library may lack the block-scaled path
+        return {"error": f"{type(ex).__name__}: {str(ex)[:200]}"}
+    return {"M": M, "N": N, "K": K, "ms": ms, "tflops": tflops(M, N, K, ms), "via": "torch._scaled_mm (hipBLASLt)"}
+
+
 def bench_layer(torch, mx, W, args):
     """One MoE layer's expert computation, forward + backward, on the gate+up /
     down workloads' routing (32768 rows, H 7168, I 2048, 16 experts): per-stage
@@ -350,6 +373,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-gemm", action="store_true", help="skip the grouped-GEMM section")
     ap.add_argument("--no-layer", action="store_true", help="skip the MoE-layer chain")
+    ap.add_argument("--vendor-baseline", action="store_true",
+                    help="also time torch._scaled_mm (hipBLASLt) MXFP8 on the dense 65536 x 2048 x 7168 GEMM")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=32768, help="rows of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -378,6 +403,7 @@ def main():
     quant, sample = bench_quant(torch, mx, W, args)
     gemm = None if args.no_gemm else bench_gemm(torch, mx, W, args)
     layer = None if args.no_layer else bench_layer(torch, mx, W, args)
+    vendor = bench_vendor(torch, W, args) if args.vendor_baseline else None
     cpu = None if sample is None else cpu_baseline(sample, args.seed)
 
     ms_step = quant["ms_rows"] + quant["ms_cols"]
@@ -413,6 +439,8 @@ def main():
         "gemm": gemm,
         "moe_layer": layer,
     }
+    if vendor is not None:
+        line["vendor_dense_mxfp8"] = vendor
     print(json.dumps(line), flush=True)
 
 
