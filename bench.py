@@ -130,7 +130,46 @@ def cpu_baseline(x_cpu_rows, seed):
     tbs = 2 * quant_bytes(M, K) / (t_rows + t_cols) / 1e12
     return {"value": tbs, "unit": "TB/s", "cores": cores, "kind": "oracle",
             "sample": f"{M} rows x {K} of the quantize workload (seed {seed}), row-wise then column-wise pass; "
-                      f"{t_rows:.2f} s + {t_cols:.2f} s wall"}
+                      f"{t_rows:.2f} s + {t_cols:.2f} s wall",
+            "gemm_oracle": gemm_oracle_rate(seed, cores)}
+
+
+def gemm_oracle_rate(seed, cores):
+    """The fp64 grouped-GEMM oracle on the tiny MoE workload in full (33.6
+    MFLOP, rows split over host threads), as GFLOP/s."""
+    import numpy as np
+    import oracle
+    from mxfp8_block_scaled_04_amd import workloads as W
+
+    d = W.tiny_moe(seed=seed, device="cpu")
+    G, N, K, M = d["G"], d["N"], d["K"], d["M"]
+    xb = d["x"].contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
+    wb = d["w"].reshape(G * N, K).contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
+    Xq, Xs = oracle.quantize_rows(xb)
+    Wq, Ws = oracle.quantize_rows(wb)
+    Wq, Ws = Wq.reshape(G, N, K), Ws.reshape(G, N, K // 32)
+    off = d["offsets"]
+    rows = np.arange(M)
+    parts = np.array_split(rows, cores)
+    t0 = time.perf_counter()
+    with concurrent.futures.ThreadPoolExecutor(cores) as ex:
+        list(ex.map(lambda r: oracle.grouped_gemm_points(Xq, Xs, Wq, Ws, off, np.repeat(r, N),
+                                                          np.tile(np.arange(N), len(r))), parts))
+    t = time.perf_counter() - t0
+    return {"gflops": 2.0 * M * N * K / t / 1e9, "s": t, "cores": cores,
+            "sample": f"tiny MoE workload in full: {M} x {N} x {K}, {G} experts (seed {seed})"}
+
+
+def launch_stats(torch, fn, n):
+    """Median / min / max of n launches, one event pair each."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    evs[-1][1].synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    return {"median": ts[len(ts) // 2], "min": ts[0], "max": ts[-1], "n": n}
 
 
 def bench_quant(torch, mx, W, args):
@@ -163,12 +202,24 @@ def bench_quant(torch, mx, W, args):
     ms_dual = tm.run(dual, args.steps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # per-launch spread (an event pair around each launch)
+    spread = {name: launch_stats(torch, fn, args.steps) for name, fn in (("rows", rows), ("cols", cols))}
+    # measured streaming ceiling: mx_stream21 reads the whole input and
+    # writes half its bytes (the quantizers' 2:1 ratio, no arithmetic)
+    flat = x.view(-1).view(torch.uint8)
+    dst = torch.empty(flat.numel() // 2, dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        mx.mx_stream21(flat, dst)
+    ms_copy = tm.run(lambda: mx.mx_stream21(flat, dst), args.steps)
+    copy_tbs = (flat.numel() + dst.numel()) / ms_copy / 1e9
+    del dst, flat
     nbytes = quant_bytes(M, K)
     dual_bytes = 2 * M * K + 2 * (M * K + M * K // 32)  # one read, both results written
     res = {
         "M": M, "K": K, "ms_rows": ms_rows, "ms_cols": ms_cols, "wall_s": wall,
         "bytes_per_pass": nbytes,
         "tbs_rows": nbytes / ms_rows / 1e9, "tbs_cols": nbytes / ms_cols / 1e9,
+        "launch_ms": spread, "copy_tbs": copy_tbs,
         "dual": {"ms": ms_dual, "bytes": dual_bytes, "tbs": dual_bytes / ms_dual / 1e9,
                  "frac_hbm_peak": dual_bytes / ms_dual / 1e9 / HBM_PEAK_TBS,
                  "ms_rows_plus_cols": ms_rows + ms_cols, "speedup_vs_two_passes": (ms_rows + ms_cols) / ms_dual},
@@ -245,7 +296,11 @@ def bench_gemm(torch, mx, W, args):
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     ms_g = timed(lambda: mx.mx_grouped_gemm(Xq, Xs, Wq, Ws, off, out=y))
     ms_d = timed(lambda: mx.mx_grouped_gemm(Xq, Xs, Dq, Ds, off1, out=y))
+    # roofline of this shape: the larger of the MFMA time and the time to
+    # stream the fp8 weights once (the case sits near the ridge point)
+    roof_ms = max(2.0 * M * N * K / (MFMA_FP8_PEAK_TFLOPS * 1e12), G * N * K * (1 + 1 / 32) / (HBM_PEAK_TBS * 1e12)) * 1e3
     out["ragged"] = {"M": M, "N": N, "K": K, "G": G, "ms_grouped": ms_g, "ms_dense": ms_d,
+                     "roofline_ms": roof_ms, "frac_roofline_grouped": roof_ms / ms_g,
                      "tflops_grouped": tflops(M, N, K, ms_g), "tflops_dense": tflops(M, N, K, ms_d),
                      "grouped_over_dense": ms_g / ms_d,
                      "frac_mfma_peak_grouped": tflops(M, N, K, ms_g) / MFMA_FP8_PEAK_TFLOPS}
@@ -430,6 +485,8 @@ def main():
                    "seed": args.seed, "frac_hbm_peak": value / HBM_PEAK_TBS,
                    "tbs_rows": quant["tbs_rows"], "tbs_cols": quant["tbs_cols"],
                    "ms_rows": quant["ms_rows"], "ms_cols": quant["ms_cols"],
+                   "launch_ms": quant["launch_ms"], "copy_tbs_measured": quant["copy_tbs"],
+                   "frac_copy_ceiling": value / quant["copy_tbs"],
                    "source_sha256": digest},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_TBS * 1000,
                      "unit": "GB/s", "frac": achieved / (HBM_PEAK_TBS * 1000), "traffic": traffic,

@@ -239,6 +239,20 @@ mx_status mx_grouped_gemm_wgrad(const uint8_t* A, const uint8_t* As, const uint8
 mx_status mx_swiglu_backward(const uint16_t* preact, const uint16_t* dh, int64_t M, int64_t I,
                              uint16_t* dpre, uint16_t* h, void* stream);
 
+/*
+ * HBM calibration stream (measurement only; not a step of the method):
+ * reads 2 * dst_bytes from src and writes dst_bytes to dst, the 2:1
+ * read:write ratio of bf16 -> fp8 quantization and its access pattern,
+ * with no arithmetic beyond an XOR: 8-byte granule i of dst = 32-bit words
+ * 0 ^ 1 and 2 ^ 3 of 16-byte granule i of src.
+ * Its rate is the practical streaming ceiling that the quantize kernels are
+ * reported against (next to the 8 TB/s specification; the quantize-bandwidth
+ * benchmark of lpnh.cn 2479732 section 4 counts bytes the same way).
+ * Requires dst_bytes % 16 == 0 (MX_ERR_SHAPE), 16-byte aligned pointers;
+ * src holds 2 * dst_bytes bytes.
+ */
+mx_status mx_stream21(const void* src, void* dst, int64_t dst_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -53,6 +53,8 @@ def load():
     lib.mx_grouped_gemm_swiglu.restype = ST
     lib.mx_swiglu_backward.argtypes = [P, P, I64, I64, P, P, P]
     lib.mx_swiglu_backward.restype = ST
+    lib.mx_stream21.argtypes = [P, P, I64, P]
+    lib.mx_stream21.restype = ST
     lib.mx_grouped_gemm_dgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, I64, P, P]
     lib.mx_grouped_gemm_dgrad.restype = ST
     lib.mx_grouped_gemm_wgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, P]
@@ -65,7 +67,7 @@ def load():
 SYMBOLS = (
     "mx_status_str", "mx_version", "mx_scale_bytes", "mx_cols_capacity", "mx_quantize_rows",
     "mx_quantize_cols", "mx_quantize_dual", "mx_grouped_gemm", "mx_grouped_gemm_swiglu", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad",
-    "mx_swiglu_backward",
+    "mx_swiglu_backward", "mx_stream21",
 )
 
 
@@ -234,6 +236,17 @@ def mx_swiglu_backward(preact, dh, dpre=None, h=None, stream=None):
                                    _stream(stream))
     _check(rc, "mx_swiglu_backward")
     return dpre, h
+
+
+def mx_stream21(src, dst, stream=None):
+    """Calibration stream: reads all of src (2x dst's bytes), writes dst."""
+    if src.numel() * src.element_size() != 2 * dst.numel() * dst.element_size():
+        raise ValueError("src must hold twice dst's bytes")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("contiguous tensors required")
+    rc = load().mx_stream21(_ptr(src), _ptr(dst), dst.numel() * dst.element_size(), _stream(stream))
+    _check(rc, "mx_stream21")
+    return dst
 
 
 def mx_grouped_gemm_dgrad(dYq, dYs, WTq, WTs, group_offsets, G, out=None, stream=None):

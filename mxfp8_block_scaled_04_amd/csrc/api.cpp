@@ -181,4 +181,13 @@ mx_status mx_swiglu_backward(const uint16_t* preact, const uint16_t* dh, int64_t
     return from_hip(mx::launch_swiglu_backward(preact, dh, M, I, dpre, h, (hipStream_t)stream));
 }
 
+mx_status mx_stream21(const void* src, void* dst, int64_t dst_bytes, void* stream) {
+    if (dst_bytes < 0 || dst_bytes % 16 != 0) return MX_ERR_SHAPE;
+    if (dst_bytes == 0) return MX_OK;
+    if (!src || !dst) return MX_ERR_NULL;
+    if (!aligned16(src) || !aligned16(dst)) return MX_ERR_ALIGN;
+    if (dst_bytes / 8 / 512 >= ((int64_t)1 << 31)) return MX_ERR_UNSUPPORTED;
+    return from_hip(mx::launch_stream21(src, dst, dst_bytes, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -129,6 +129,15 @@ def test_swiglu_backward_validation():
     assert f(None, None, 0, 64, None, None, None) == 0             # M == 0: no work
 
 
+def test_stream21_validation():
+    f = mx.load().mx_stream21
+    assert f(FAKE, FAKE, 24, None) == 2                    # not a multiple of 16 bytes
+    assert f(FAKE, FAKE, -16, None) == 2
+    assert f(None, FAKE, 64, None) == 1
+    assert f(FAKE, P(0x100004), 64, None) == 3
+    assert f(None, None, 0, None) == 0
+
+
 def test_dgrad_validation():
     f = mx.load().mx_grouped_gemm_dgrad
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 64, 512, 1024, FAKE, None) == 4   # Wcap < G*K

@@ -153,3 +153,15 @@ def test_cols_down_backward_sampled():
         assert np.array_equal(u8(qT[torch.from_numpy(cols).to(DEV)]), q_ref)
         s_all = canonical_scales(sT, N, Mcap)
         assert np.array_equal(s_all[cols], s_ref)
+
+
+def test_stream21_calibration_kernel():
+    """The calibration stream: 8-byte granule i of dst = words 0^1, 2^3 of src granule i."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, ((3 * 4096 + 7) * 8,), dtype=torch.int32, device=DEV, generator=g)
+    dst = torch.full((src.numel() // 2,), -1, dtype=torch.int32, device=DEV)
+    mx.mx_stream21(src, dst)
+    torch.cuda.synchronize()
+    s4 = src.view(-1, 4)
+    assert torch.equal(dst.view(-1, 2), torch.stack([s4[:, 0] ^ s4[:, 1], s4[:, 2] ^ s4[:, 3]], dim=1))
