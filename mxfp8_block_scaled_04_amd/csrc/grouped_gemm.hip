@@ -89,7 +89,15 @@ __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][TM * SK];
 __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][TN * SK];
 __shared__ __attribute__((aligned(16))) uint32_t lds_sa[2][TM / 32][64];  // scale dwords, [chunk parity][32-row unit][lane]
 __shared__ __attribute__((aligned(16))) uint32_t lds_sb[2][TN / 32][64];
-__shared__ int32_t tile_end[kMaxGroups];  // inclusive prefix of tiles per group
+__shared__ int32_t tile_end[kMaxGroups];  // inclusive prefix of tiles per group (position order)
+// wgrad with at most kLptGroups groups: its tiles cost in proportion to their
+// group's contraction length, so groups are taken longest first (lpt_order[k]
+// = the group at position k) and workgroups take the tiles of successive
+// rounds in alternating directions, which balances the per-workgroup sums
+constexpr int kLptGroups = 256;
+__shared__ int32_t lpt_order[kLptGroups];
+
+__device__ __forceinline__ bool lpt_mode(const GemmArgs& a) { return a.mode == 1 && a.G <= kLptGroups; }
 
 __device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
     return v < lo ? lo : (v > hi ? hi : v);
@@ -406,6 +414,7 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& a, const Layout& L, 
     g = (int)uni((uint32_t)g);
     const int64_t first = g > 0 ? tile_end[g - 1] : 0;
     const int64_t local = tile - first;
+    const int grp = (int)uni((uint32_t)(lpt_mode(a) ? lpt_order[g] : g));  // g: position in tile order
     const uint8_t *B0, *Bs0;
     int64_t arows, brows, k0, k1, arow0, brow0;
     if (a.mode != 1) {
@@ -452,8 +461,8 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& a, const Layout& L, 
         const int64_t r = local - band * kBand * nNt;
         const int64_t mt = band * kBand + r % gm;
         const int64_t nt = r / gm;
-        k0 = clamp64(a.offsets[g], 0, a.Mcap) & ~(int64_t)255;
-        k1 = clamp64(a.offsets[g + 1], 0, a.Mcap) & ~(int64_t)255;
+        k0 = clamp64(a.offsets[grp], 0, a.Mcap) & ~(int64_t)255;
+        k1 = clamp64(a.offsets[grp + 1], 0, a.Mcap) & ~(int64_t)255;
         if (k1 < k0) k1 = k0;
         arow0 = mt * TM;
         arows = a.N - arow0;
@@ -461,7 +470,7 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& a, const Layout& L, 
         brows = a.K - brow0;
         B0 = a.B;
         Bs0 = a.Bs;
-        T.outoff = (int64_t)g * a.N * a.K + arow0 * a.K + nt * TN;
+        T.outoff = (int64_t)grp * a.N * a.K + arow0 * a.K + nt * TN;
         T.rows = (int32_t)(arows < TM ? arows : TM);
         T.cols = (int32_t)(brows < TN ? brows : TN);
     }
@@ -668,6 +677,24 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs a) {
     const int G = a.G;
     const int64_t nN = (a.N + TN - 1) / TN;
     const int64_t per1 = ((a.N + TM - 1) / TM) * ((a.K + TN - 1) / TN);
+    const bool lpt = lpt_mode(a);
+    if (lpt) {
+        // rank the groups by contraction length, longest first (ties by index)
+        __shared__ int32_t lpt_len[kLptGroups];
+        if (t < G) {
+            const int64_t p0 = clamp64(a.offsets[t], 0, a.Mcap) & ~(int64_t)255;
+            const int64_t p1 = clamp64(a.offsets[t + 1], 0, a.Mcap) & ~(int64_t)255;
+            lpt_len[t] = p1 > p0 ? (int32_t)((p1 - p0) >> 8) : 0;
+        }
+        __syncthreads();
+        if (t < G) {
+            const int32_t c = lpt_len[t];
+            int rank = 0;
+            for (int h = 0; h < G; ++h) rank += (lpt_len[h] > c || (lpt_len[h] == c && h < t)) ? 1 : 0;
+            lpt_order[rank] = t;
+        }
+        __syncthreads();
+    }
     {
         int32_t loc[16];
         int32_t sum = 0;
@@ -681,8 +708,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs a) {
                     const int64_t mg = hi > lo ? hi - lo : 0;
                     cnt = (int32_t)(((mg + TM - 1) / TM) * nN);
                 } else {
-                    const int64_t p0 = clamp64(a.offsets[g], 0, a.Mcap) & ~(int64_t)255;
-                    const int64_t p1 = clamp64(a.offsets[g + 1], 0, a.Mcap) & ~(int64_t)255;
+                    const int gg = lpt ? lpt_order[g] : g;
+                    const int64_t p0 = clamp64(a.offsets[gg], 0, a.Mcap) & ~(int64_t)255;
+                    const int64_t p1 = clamp64(a.offsets[gg + 1], 0, a.Mcap) & ~(int64_t)255;
                     cnt = p1 > p0 ? (int32_t)per1 : 0;
                 }
             }
@@ -719,7 +747,12 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs a) {
         wait_vm<0>();
     }
 
+    // round r gives workgroup slot the tile r nwg + slot, or r nwg + nwg - 1 -
+    // slot in odd rounds when the groups are taken longest first: from an even
+    // round the next tile is 2 (nwg - slot) - 1 further, from an odd one
+    // 2 slot + 1
     int64_t tile = slot;
+    bool odd = false;
     if (tile >= total) return;
 
     // per-lane constants
@@ -784,7 +817,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs a) {
             run_chunk<kEpiWait>(P, acc, X, c == 0 && !first && kEpiWait > 0, Ln, L, w, l, wm, wn, la0, la1, lb0,
                                 lb1);
         }
-        const Tile Tn = decode_tile<EPI>(a, L, tile + nwg, total, gcur);
+        const int64_t next = tile + (!lpt ? nwg : odd ? 2 * slot + 1 : 2 * (nwg - slot) - 1);
+        const Tile Tn = decode_tile<EPI>(a, L, next, total, gcur);
         {
             const Ahead X{Tn.ra, Tn.rb, Tn.rsa, Tn.rsb, Tn.asub, Tn.bsub, uni(0u), uni(0u), uni((uint32_t)SK)};
             run_chunk<kEpiWait>(P, acc, X, c == 0 && !first && kEpiWait > 0, Ln, L, w, l, wm, wn, la0, la1, lb0,
@@ -817,7 +851,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs a) {
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
         if (Tn.nchunk == 0) break;
         T = Tn;
-        tile += nwg;
+        tile = next;
+        odd = !odd;
         first = false;
     }
     // Loads through empty descriptors and the last stores: let them finish
