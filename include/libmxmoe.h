@@ -240,6 +240,17 @@ mx_status mx_swiglu_backward(const uint16_t* preact, const uint16_t* dh, int64_t
                              uint16_t* dpre, uint16_t* h, void* stream);
 
 /*
+ * Device-side check of a group_offsets array, for callers that want to
+ * verify it (the kernels clamp malformed offsets instead of reading out of
+ * bounds): valid means 0 <= o[0] <= o[1] <= ... <= o[G] <= M (rows outside
+ * [o[0], o[G]) belong to no group).  Writes result[0] (int32, device) = 0 if
+ * valid, else 1 + the first index that breaks the rule; asynchronous like
+ * every call.  1 <= G <= 4096, M >= 0 (MX_ERR_SHAPE).
+ */
+mx_status mx_validate_offsets(const int32_t* group_offsets, int32_t G, int64_t M, int32_t* result,
+                              void* stream);
+
+/*
  * HBM calibration stream (measurement only; not a step of the method):
  * reads 2 * dst_bytes from src and writes dst_bytes to dst, the 2:1
  * read:write ratio of bf16 -> fp8 quantization and its access pattern,

@@ -53,6 +53,8 @@ def load():
     lib.mx_grouped_gemm_swiglu.restype = ST
     lib.mx_swiglu_backward.argtypes = [P, P, I64, I64, P, P, P]
     lib.mx_swiglu_backward.restype = ST
+    lib.mx_validate_offsets.argtypes = [P, I32, I64, P, P]
+    lib.mx_validate_offsets.restype = ST
     lib.mx_stream21.argtypes = [P, P, I64, P]
     lib.mx_stream21.restype = ST
     lib.mx_grouped_gemm_dgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, I64, P, P]
@@ -67,7 +69,7 @@ def load():
 SYMBOLS = (
     "mx_status_str", "mx_version", "mx_scale_bytes", "mx_cols_capacity", "mx_quantize_rows",
     "mx_quantize_cols", "mx_quantize_dual", "mx_grouped_gemm", "mx_grouped_gemm_swiglu", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad",
-    "mx_swiglu_backward", "mx_stream21",
+    "mx_swiglu_backward", "mx_validate_offsets", "mx_stream21",
 )
 
 
@@ -236,6 +238,17 @@ def mx_swiglu_backward(preact, dh, dpre=None, h=None, stream=None):
                                    _stream(stream))
     _check(rc, "mx_swiglu_backward")
     return dpre, h
+
+
+def mx_validate_offsets(group_offsets, M, result=None, stream=None):
+    """Device check of group offsets: returns an int32 device tensor [1] holding
+    0 if 0 <= o[0] <= ... <= o[G] <= M, else 1 + the first bad index."""
+    if result is None:
+        result = torch.empty(1, dtype=torch.int32, device=group_offsets.device)
+    rc = load().mx_validate_offsets(_ptr(group_offsets), group_offsets.numel() - 1, M, _ptr(result),
+                                    _stream(stream))
+    _check(rc, "mx_validate_offsets")
+    return result
 
 
 def mx_stream21(src, dst, stream=None):

@@ -181,6 +181,12 @@ mx_status mx_swiglu_backward(const uint16_t* preact, const uint16_t* dh, int64_t
     return from_hip(mx::launch_swiglu_backward(preact, dh, M, I, dpre, h, (hipStream_t)stream));
 }
 
+mx_status mx_validate_offsets(const int32_t* group_offsets, int32_t G, int64_t M, int32_t* result, void* stream) {
+    if (G < 1 || G > kMaxGroups || M < 0) return MX_ERR_SHAPE;
+    if (!group_offsets || !result) return MX_ERR_NULL;
+    return from_hip(mx::launch_validate_offsets(group_offsets, G, M, result, (hipStream_t)stream));
+}
+
 mx_status mx_stream21(const void* src, void* dst, int64_t dst_bytes, void* stream) {
     if (dst_bytes < 0 || dst_bytes % 16 != 0) return MX_ERR_SHAPE;
     if (dst_bytes == 0) return MX_OK;

@@ -37,6 +37,9 @@ hipError_t launch_grouped_gemm_wgrad(const uint8_t* A, const uint8_t* As, const 
 hipError_t launch_swiglu_backward(const uint16_t* preact, const uint16_t* dh, int64_t M, int64_t I, uint16_t* dpre,
                                   uint16_t* h, hipStream_t stream);
 
+hipError_t launch_validate_offsets(const int32_t* offsets, int32_t G, int64_t M, int32_t* result,
+                                  hipStream_t stream);
+
 hipError_t launch_stream21(const void* src, void* dst, int64_t dst_bytes, hipStream_t stream);
 
 }  // namespace mx

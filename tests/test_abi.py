@@ -129,6 +129,15 @@ def test_swiglu_backward_validation():
     assert f(None, None, 0, 64, None, None, None) == 0             # M == 0: no work
 
 
+def test_validate_offsets_argument_errors():
+    f = mx.load().mx_validate_offsets
+    assert f(FAKE, 0, 100, FAKE, None) == 2        # G < 1
+    assert f(FAKE, 4097, 100, FAKE, None) == 2     # G too large
+    assert f(FAKE, 4, -1, FAKE, None) == 2         # M < 0
+    assert f(None, 4, 100, FAKE, None) == 1
+    assert f(FAKE, 4, 100, None, None) == 1
+
+
 def test_stream21_validation():
     f = mx.load().mx_stream21
     assert f(FAKE, FAKE, 24, None) == 2                    # not a multiple of 16 bytes

@@ -230,3 +230,17 @@ def test_wgrad_down_backward_sampled():
     got = bf16_to_f64(dW[torch.from_numpy(gs).to(DEV), torch.from_numpy(ns).to(DEV), torch.from_numpy(ks).to(DEV)])
     ok, ratio = gemm_tolerance_ok(got, ref)
     assert ok, ratio
+
+
+@pytest.mark.parametrize("offs,M,want", [
+    ([0, 160, 160, 256, 512], 512, 0),      # the tiny MoE routing
+    ([16, 76, 76, 150], 170, 0),            # rows outside every group are allowed
+    ([0, 10, 5, 20], 20, 3),                # decreasing at index 2
+    ([-1, 5, 9], 9, 1),                     # negative first entry
+    ([0, 5, 11], 10, 3),                    # past M
+    ([0] * 4097, 0, 0),                     # 4096 empty groups
+])
+def test_validate_offsets(offs, M, want):
+    r = mx.mx_validate_offsets(torch.tensor(offs, dtype=torch.int32, device=DEV), M)
+    torch.cuda.synchronize()
+    assert int(r.item()) == want
