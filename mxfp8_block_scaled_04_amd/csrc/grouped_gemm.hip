@@ -732,7 +732,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs a) {
             if (t * 16 + j < G) tile_end[t * 16 + j] = base + loc[j];
         __syncthreads();
     }
-    const int64_t total = G > 0 ? tile_end[G - 1] : 0;
+    // (a count below 2^31 read from LDS, made wave-uniform so that what is
+    // derived from it stays in scalar registers)
+    const int64_t total = (int64_t)uni((uint32_t)(G > 0 ? tile_end[G - 1] : 0));
 
     if (a.mode == 1) {
         // groups with an empty contraction range: dW[g] = 0
