@@ -244,3 +244,55 @@ def test_validate_offsets(offs, M, want):
     r = mx.mx_validate_offsets(torch.tensor(offs, dtype=torch.int32, device=DEV), M)
     torch.cuda.synchronize()
     assert int(r.item()) == want
+
+
+def test_wgrad_many_groups_natural_order():
+    """300 groups (above the 256 that are ranked longest first): the natural
+    tile order; mixed lengths, empty groups; sampled against the oracle."""
+    rng = np.random.default_rng(21)
+    sizes = list(rng.choice([0, 1, 40, 300, 600], 300))
+    M, N, K = int(sum(sizes)), 64, 96
+    off = W.offsets_from_sizes(sizes)
+    dy = W.normal_bf16((M, N), 1.0, 31, DEV)
+    x = W.normal_bf16((M, K), 1.0, 32, DEV)
+    off_dev = torch.from_numpy(off).to(DEV)
+    A, As, P = mx.mx_quantize_cols(dy, off_dev)
+    B, Bs, _ = mx.mx_quantize_cols(x, off_dev)
+    G = len(sizes)
+    dW = mx.mx_grouped_gemm_wgrad(A, As, B, Bs, P, dW=nan_filled((G, N, K)))
+    torch.cuda.synchronize()
+    Mcap = A.shape[1]
+    Aq, Asc, Pr = oracle.quantize_cols(bits(dy), off, Mcap)
+    Bq, Bsc, _ = oracle.quantize_cols(bits(x), off, Mcap)
+    gs = rng.integers(0, G, 3000)
+    ns = rng.integers(0, N, 3000)
+    ks = rng.integers(0, K, 3000)
+    ref = oracle.wgrad_points(Aq, Asc, Bq, Bsc, Pr, gs, ns, ks)
+    got = bf16_to_f64(dW)[gs, ns, ks]
+    ok, ratio = gemm_tolerance_ok(got, ref)
+    assert ok, ratio
+    empty = [g for g in range(G) if sizes[g] == 0]
+    assert torch.count_nonzero(dW[empty].float()).item() == 0
+
+
+def test_gemm_4096_groups():
+    """The largest group count: 4096 experts, most of them empty, a few with
+    1-300 rows; every output row of a group checked at sampled columns."""
+    rng = np.random.default_rng(22)
+    G, N, K = 4096, 128, 256
+    sizes = np.zeros(G, np.int64)
+    busy = rng.choice(G, 40, replace=False)
+    sizes[busy] = rng.integers(1, 300, 40)
+    M = int(sizes.sum())
+    off = W.offsets_from_sizes(list(sizes))
+    x = W.normal_bf16((M, K), 1.0, 33, DEV)
+    w = W.normal_bf16((G, N, K), 0.02, 34, DEV)
+    Xq, Xs, Wq, Ws = quantize_pair(x, w)
+    out = mx.mx_grouped_gemm(Xq, Xs, Wq, Ws, torch.from_numpy(off).to(DEV), out=nan_filled((M, N)))
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any().item()
+    rows = np.arange(M)
+    cols = rng.integers(0, N, M)
+    ref = oracle.grouped_gemm_points(*host_operands(Xq, Xs, Wq, Ws), off, rows, cols)
+    ok, ratio = gemm_tolerance_ok(bf16_to_f64(out)[rows, cols], ref)
+    assert ok, ratio
