@@ -131,7 +131,8 @@ def cpu_baseline(x_cpu_rows, seed):
     return {"value": tbs, "unit": "TB/s", "cores": cores, "kind": "oracle",
             "sample": f"{M} rows x {K} of the quantize workload (seed {seed}), row-wise then column-wise pass; "
                       f"{t_rows:.2f} s + {t_cols:.2f} s wall",
-            "gemm_oracle": gemm_oracle_rate(seed, cores)}
+            "gemm_oracle": gemm_oracle_rate(seed, cores),
+            "gemm_oracle_gate_up": gemm_oracle_gate_up_sample(seed, cores)}
 
 
 def gemm_oracle_rate(seed, cores):
@@ -158,6 +159,63 @@ def gemm_oracle_rate(seed, cores):
     t = time.perf_counter() - t0
     return {"gflops": 2.0 * M * N * K / t / 1e9, "s": t, "cores": cores,
             "sample": f"tiny MoE workload in full: {M} x {N} x {K}, {G} experts (seed {seed})"}
+
+
+def gemm_oracle_gate_up_sample(seed, cores, device="cuda"):
+    """The fp64 grouped-GEMM oracle on a deterministic sample of the gate+up
+    workload (32768 x 4096 x 7168, 16 experts): a 128 x 128 output patch at
+    the start of every non-empty group (clipped to the group) plus 4096
+    uniform points.  The oracle quantizes the bf16 operands first (not
+    timed); the points are split over host threads.  Reported as GFLOP/s of
+    the sample and the full GEMM's time extrapolated at that rate."""
+    import numpy as np
+    import torch
+    import oracle
+    from mxfp8_block_scaled_04_amd import workloads as W
+
+    d = W.moe_gate_up(seed=seed, device=device)
+    G, N, K, M = d["G"], d["N"], d["K"], d["M"]
+    off = d["offsets"]
+
+    def host_bits(t):
+        return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    xb = host_bits(d["x"])
+    wb = host_bits(d["w"].reshape(G * N, K))
+    del d
+
+    def quant_all(bits):
+        parts = np.array_split(np.arange(bits.shape[0]), cores)
+        with concurrent.futures.ThreadPoolExecutor(cores) as ex:
+            res = list(ex.map(lambda r: oracle.quantize_rows(bits[r[0]:r[-1] + 1]), parts))
+        return np.concatenate([q for q, _ in res]), np.concatenate([s for _, s in res])
+
+    Xq, Xs = quant_all(xb)
+    del xb
+    Wq, Ws = quant_all(wb)
+    del wb
+    Wq, Ws = Wq.reshape(G, N, K), Ws.reshape(G, N, K // 32)
+    rng = np.random.default_rng(seed)
+    rows = [rng.integers(0, M, 4096)]
+    cols = [rng.integers(0, N, 4096)]
+    for g in range(G):
+        lo, hi = int(off[g]), int(off[g + 1])
+        if hi <= lo:
+            continue
+        r = np.arange(lo, min(lo + 128, hi))
+        rows.append(np.repeat(r, 128))
+        cols.append(np.tile(np.arange(128), r.size))
+    rows, cols = np.concatenate(rows).astype(np.int64), np.concatenate(cols).astype(np.int64)
+    parts = np.array_split(np.arange(rows.size), cores)
+    t0 = time.perf_counter()
+    with concurrent.futures.ThreadPoolExecutor(cores) as ex:
+        list(ex.map(lambda p: oracle.grouped_gemm_points(Xq, Xs, Wq, Ws, off, rows[p], cols[p]), parts))
+    t = time.perf_counter() - t0
+    rate = 2.0 * rows.size * K / t
+    return {"gflops": rate / 1e9, "s": t, "cores": cores, "points": int(rows.size),
+            "extrapolated_full_s": 2.0 * M * N * K / rate,
+            "sample": f"gate+up workload {M} x {N} x {K}, {G} experts (seed {seed}): a 128 x 128 patch per "
+                      f"non-empty group + 4096 uniform points; full-size time extrapolated, not measured"}
 
 
 def launch_stats(torch, fn, n):

@@ -155,6 +155,26 @@ def test_cols_down_backward_sampled():
         assert np.array_equal(s_all[cols], s_ref)
 
 
+def test_cols_quant_bandwidth_sampled():
+    """The quantize-bandwidth workload [131072, 7168] column-wise with no
+    groups, as the benchmark runs it: a grid of 512 x 112 workgroups, which
+    takes the 256-thread variant of the kernel (smaller grids take the
+    512-thread one).  Sampled transposed rows (= columns of x), all 131072
+    positions each, against the oracle."""
+    x = W.quant_bandwidth(seed=0, device=DEV)
+    M, N = x.shape
+    qT, sT, P = mx.mx_quantize_cols(x)
+    torch.cuda.synchronize()
+    Mcap = qT.shape[1]
+    assert Mcap == M and (Mcap // 256) * ((N + 63) // 64) >= 32768
+    cols = np.unique(np.concatenate([[0, 1, 63, 64, N - 1], np.random.default_rng(2).integers(0, N, 24)]))
+    idx = torch.from_numpy(cols).to(DEV)
+    q_ref, s_ref, _ = oracle.quantize_cols(bits(x[:, idx]), None, Mcap)
+    assert np.array_equal(u8(qT[idx]), q_ref)
+    s_all = canonical_scales(sT, N, Mcap)
+    assert np.array_equal(s_all[cols], s_ref)
+
+
 def test_stream21_calibration_kernel():
     """The calibration stream: 8-byte granule i of dst = words 0^1, 2^3 of src granule i."""
     g = torch.Generator(device=DEV)
