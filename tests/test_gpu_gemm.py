@@ -99,6 +99,34 @@ def test_gemm_ragged_full(sizes, N, K):
     assert ok, ratio
 
 
+def test_gemm_group_permutation_bitwise():
+    """Experts permuted together with their row blocks permute the output row
+    blocks bit for bit: a row's result depends on its expert and its data,
+    not on where its group sits (row tiles, bands, workgroups, XCDs).  Group
+    sizes put rows at every offset mod 256 and mix full, partial and empty
+    row tiles."""
+    sizes = [300, 0, 45, 513, 7, 128, 129, 256, 1]
+    G, N, K = len(sizes), 384, 512
+    M = sum(sizes)
+    off = W.offsets_from_sizes(sizes)
+    x = W.normal_bf16((M, K), 1.0, 11, DEV)
+    w = W.normal_bf16((G, N, K), 0.02, 12, DEV)
+    perm = np.random.default_rng(3).permutation(G)
+    sizes_p = [sizes[g] for g in perm]
+    off_p = W.offsets_from_sizes(sizes_p)
+    rows_p = np.concatenate([np.arange(off[g], off[g + 1]) for g in perm]).astype(np.int64)
+    x_p = x[torch.from_numpy(rows_p).to(DEV)].contiguous()
+    w_p = w[torch.from_numpy(perm).to(DEV)].contiguous()
+    outs = []
+    for xx, ww, oo in ((x, w, off), (x_p, w_p, off_p)):
+        Xq, Xs, Wq, Ws = quantize_pair(xx, ww)
+        outs.append(mx.mx_grouped_gemm(Xq, Xs, Wq, Ws, torch.from_numpy(oo).to(DEV), out=nan_filled((M, N))))
+    torch.cuda.synchronize()
+    a = bits(outs[0])[rows_p]
+    b = bits(outs[1])
+    assert np.array_equal(a, b), int(np.count_nonzero(a != b))
+
+
 def test_gemm_zero_rows_is_noop():
     Xq = torch.empty((0, 256), dtype=torch.uint8, device=DEV)
     Xs = torch.empty(0, dtype=torch.uint8, device=DEV)
