@@ -49,8 +49,9 @@ mx_status mx_quantize_rows(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
     if (M == 0 || K == 0) return MX_OK;
     if (!x || !q || !s) return MX_ERR_NULL;
     if (!aligned16(x) || !aligned16(q) || !aligned16(s) || ldx % 8 != 0) return MX_ERR_ALIGN;
-    // one 256-thread workgroup per 32 x 256 unit; total work-items < 2^32
-    if (((M + 31) / 32) * ((K + 255) / 256) > (int64_t)(UINT32_MAX / 256)) return MX_ERR_UNSUPPORTED;
+    // one workgroup of kQuantRowsThreads per 32 x 256 unit; total work-items < 2^32
+    if (((M + 31) / 32) * ((K + 255) / 256) > (int64_t)(UINT32_MAX / mx::kQuantRowsThreads))
+        return MX_ERR_UNSUPPORTED;
     return from_hip(mx::launch_quantize_rows(x, M, K, ldx, q, s, (hipStream_t)stream));
 }
 
@@ -192,7 +193,8 @@ mx_status mx_stream21(const void* src, void* dst, int64_t dst_bytes, void* strea
     if (dst_bytes == 0) return MX_OK;
     if (!src || !dst) return MX_ERR_NULL;
     if (!aligned16(src) || !aligned16(dst)) return MX_ERR_ALIGN;
-    if (dst_bytes / 8 / 512 >= ((int64_t)1 << 31)) return MX_ERR_UNSUPPORTED;
+    // one lane per 2 granules (16 bytes read, 8 written each): work-items < 2^32
+    if (dst_bytes / 16 >= ((int64_t)1 << 32) - 256) return MX_ERR_UNSUPPORTED;
     return from_hip(mx::launch_stream21(src, dst, dst_bytes, (hipStream_t)stream));
 }
 

@@ -6,6 +6,10 @@
 
 namespace mx {
 
+// Workgroup size of the row-wise quantize kernel (one workgroup per unit of
+// 32 rows x 256 columns); the entry point bounds the grid with it.
+constexpr int kQuantRowsThreads = 512;
+
 hipError_t launch_quantize_rows(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                                 uint8_t* s, hipStream_t stream);
 

@@ -23,10 +23,7 @@ namespace mx {
 // Rows >= M and blocks >= K read as zero, which yields scale 0 and keeps the
 // pad bytes of the packed scale array at 0.
 // ---------------------------------------------------------------------------
-#ifndef MX_ROWS_WAVES
-#define MX_ROWS_WAVES 8
-#endif
-constexpr int kRowsWaves = MX_ROWS_WAVES;
+constexpr int kRowsWaves = kQuantRowsThreads / 64;
 constexpr int kRowsLoads = 16 / kRowsWaves;  // 16-byte loads per lane
 static_assert(kRowsWaves == 4 || kRowsWaves == 8 || kRowsWaves == 16, "unit = 32 rows");
 

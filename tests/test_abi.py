@@ -53,6 +53,8 @@ FAKE = P(0x100000)  # never dereferenced: every call below fails validation firs
         ((P(0x100004), 4, 32, 32, FAKE, FAKE, None), 3),  # misaligned x
         ((FAKE, 4, 32, 36, FAKE, FAKE, None), 3),   # ldx not a multiple of 8
         ((None, 0, 32, 32, None, None, None), 0),   # M == 0: no work, OK
+        # 2^23 units of 32 x 256 at 512 threads each: 2^32 work-items, over the grid limit
+        ((FAKE, 32 * (1 << 23), 256, 256, FAKE, FAKE, None), 5),
     ],
 )
 def test_quantize_rows_validation(args, want):
@@ -145,6 +147,7 @@ def test_stream21_validation():
     assert f(None, FAKE, 64, None) == 1
     assert f(FAKE, P(0x100004), 64, None) == 3
     assert f(None, None, 0, None) == 0
+    assert f(FAKE, FAKE, 16 << 32, None) == 5              # 2^32 lanes: over the grid limit
 
 
 def test_dgrad_validation():
@@ -168,3 +171,4 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(mx, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError):
         mx.load()
+
