@@ -84,3 +84,27 @@ def test_dual_down_backward_sampled():
     assert np.array_equal(P.cpu().numpy(), P_ref)
     assert np.array_equal(u8(qT[torch.from_numpy(cols).to(DEV)]), qT_ref)
     assert np.array_equal(canonical_scales(sT, N, Mcap)[cols], sT_ref)
+
+
+def test_dual_quant_bandwidth_sampled():
+    """The quantize-bandwidth workload [131072, 7168] with no groups, as the
+    benchmark runs it: sampled rows of the row-wise result (every 64-column
+    sub-tile pair of each, so both halves of the jointly stored 128-byte
+    pieces) and sampled columns of the column-wise result."""
+    x = W.quant_bandwidth(seed=0, device=DEV)
+    M, N = x.shape
+    q, s, qT, sT, P = mx.mx_quantize_dual(x)
+    torch.cuda.synchronize()
+    assert P is None
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, M - 1], rng.integers(0, M, 128)]))
+    ridx = torch.from_numpy(rows).to(DEV)
+    q_ref, s_ref = oracle.quantize_rows(bits(x[ridx]))
+    assert np.array_equal(u8(q[ridx]), q_ref)
+    assert np.array_equal(canonical_scales(s, M, N)[rows], s_ref)
+    Mcap = qT.shape[1]
+    cols = np.unique(np.concatenate([[0, 63, 64, 255, 256, N - 1], rng.integers(0, N, 16)]))
+    cidx = torch.from_numpy(cols).to(DEV)
+    qT_ref, sT_ref, _ = oracle.quantize_cols(bits(x[:, cidx]), None, Mcap)
+    assert np.array_equal(u8(qT[cidx]), qT_ref)
+    assert np.array_equal(canonical_scales(sT, N, Mcap)[cols], sT_ref)
