@@ -213,8 +213,8 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(const uint1
         const uint2 c = quant8(d, S);
         const int64_t ng = nt * 64 + n;
         if (ng < N) {
-            // small grids: ordinary stores (measured 4 % faster there, 5 % slower
-            // on large grids, whose output does not stay in cache anyway)
+            // small grids: ordinary stores (measured 4 % faster there, and 5 %
+            // slower on large grids, which keep non-temporal ones)
             if (kColsThreads == 512) store8(qT + ng * Mcap + col0 + 8 * j, c);
             else store_stream8(qT + ng * Mcap + col0 + 8 * j, c);
         }
