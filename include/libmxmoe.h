@@ -87,7 +87,9 @@ int64_t mx_cols_capacity(int64_t M, int32_t G);
  *   x   bf16 [M][ldx] (first K columns used), 16-byte aligned, ldx % 8 == 0
  *   q   uint8 [M][K] codes, 16-byte aligned
  *   s   packed scales for R = M rows, contraction K (mx_scale_bytes(M, K))
- * Requires K % 32 == 0, ldx >= K.
+ * Requires K % 32 == 0, ldx >= K.  MX_ERR_UNSUPPORTED when
+ * ceil(M / 32) * ceil(K / 256) exceeds 2^23 - 1 (the launch grid would pass
+ * 2^32 work-items).
  */
 mx_status mx_quantize_rows(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                            uint8_t* s, void* stream);
@@ -260,7 +262,8 @@ mx_status mx_validate_offsets(const int32_t* group_offsets, int32_t G, int64_t M
  * reported against (next to the 8 TB/s specification; the quantize-bandwidth
  * benchmark of lpnh.cn 2479732 section 4 counts bytes the same way).
  * Requires dst_bytes % 16 == 0 (MX_ERR_SHAPE), 16-byte aligned pointers;
- * src holds 2 * dst_bytes bytes.
+ * src holds 2 * dst_bytes bytes.  MX_ERR_UNSUPPORTED from dst_bytes / 16 >=
+ * 2^32 - 256 on (one lane per 16 bytes written: the grid limit).
  */
 mx_status mx_stream21(const void* src, void* dst, int64_t dst_bytes, void* stream);
 
