@@ -179,11 +179,22 @@ __device__ __forceinline__ void bdma4(const i32x4& rs, uint32_t voff, uint32_t s
 __device__ __forceinline__ void order_between(i32x8& before, i32x8& after) {
     asm volatile("" : "+v"(before), "+v"(after) : : "memory");
 }
-// 16-byte range-checked store.
-__device__ __forceinline__ void bstore16(const i32x4& rs, uint32_t voff, uint32_t soff, i32x4 v) {
-    asm volatile("buffer_store_dwordx4 %0, %1, %2, %3 offen" ::"v"(v), "v"(voff), "s"(rs), "s"(soff) : "memory");
-}
 #pragma clang diagnostic pop
+
+// Range-checked stores go through the compiler's buffer-store builtins, never
+// inline asm: a store of more than 8 bytes reads its data registers after it
+// issues, and on gfx950 a vector ALU op may overwrite them only two wait
+// states later.  The compiler's hazard recognizer inserts those wait states
+// for stores it can see, not for stores hidden in an asm statement (a
+// 16-byte asm store whose data registers were rewritten by the next
+// instruction stored partly stale data).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t store_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void bstore16(rsrc_t rs, uint32_t voff, i32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, (int)voff, 0, 0);
+}
 
 // Wait until at most N vector-memory operations of this wave are in flight
 // (they complete in issue order).
@@ -506,8 +517,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
 template <int I0 = 0, int I1 = 4>
 __device__ __forceinline__ void epilogue16(uint16_t* out, const Tile& T, const Layout& L, f32x16 (&acc)[4][4], int wm,
                                            int wn, int h, int r32) {
-    const i32x4 ro = make_rsrc(out, (uint32_t)T.rows * L.ldo * 2u);
-    const uint32_t zero = uni(0u);
+    const rsrc_t ro = store_rsrc(out, (uint32_t)T.rows * L.ldo * 2u);
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
         const uint32_t rowoff = (uint32_t)(wm * 128 + i * 32 + r32) * L.ldo * 2u;
@@ -524,7 +534,7 @@ __device__ __forceinline__ void epilogue16(uint16_t* out, const Tile& T, const L
                 const auto sy = __builtin_amdgcn_permlane32_swap(y0, y1, false, false);
                 const int col = wn * 128 + j * 32 + 16 * p + 8 * h;
                 const uint32_t off = col < T.cols ? rowoff + (uint32_t)col * 2u : 0xFFFFFFF0u;
-                bstore16(ro, off, zero, i32x4{(int)sx[0], (int)sy[0], (int)sx[1], (int)sy[1]});
+                bstore16(ro, off, i32x4{(int)sx[0], (int)sy[0], (int)sx[1], (int)sy[1]});
             }
     }
 }
@@ -552,11 +562,11 @@ __device__ __forceinline__ float silu(float x) {
     return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.44269504088896341f));
 }
 
-__device__ __forceinline__ void bstore4(const i32x4& rs, uint32_t voff, uint32_t soff, uint32_t v) {
-    asm volatile("buffer_store_dword %0, %1, %2, %3 offen" ::"v"(v), "v"(voff), "s"(rs), "s"(soff) : "memory");
+__device__ __forceinline__ void bstore4(rsrc_t rs, uint32_t voff, uint32_t v) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, rs, (int)voff, 0, 0);
 }
-__device__ __forceinline__ void bstore1(const i32x4& rs, uint32_t voff, uint32_t soff, uint32_t v) {
-    asm volatile("buffer_store_byte %0, %1, %2, %3 offen" ::"v"(v), "v"(voff), "s"(rs), "s"(soff) : "memory");
+__device__ __forceinline__ void bstore1(rsrc_t rs, uint32_t voff, uint32_t v) {
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, rs, (int)voff, 0, 0);
 }
 
 template <int I0 = 0, int I1 = 4>
@@ -568,10 +578,9 @@ __device__ __forceinline__ void epilogue_swiglu(const GemmArgs& a, const Tile& T
     // hidden columns [128 nt, 128 nt + 128))
     const int64_t row0 = T.outoff >> 24;
     const int64_t hcol0 = (T.outoff & 0xFFFFFF) * (TN / 2);
-    const i32x4 rq = make_rsrc(a.hq + row0 * I + hcol0, (uint32_t)((int64_t)T.rows * I));
+    const rsrc_t rq = store_rsrc(a.hq + row0 * I + hcol0, (uint32_t)((int64_t)T.rows * I));
     const int64_t hs_bytes = ((a.M + 31) / 32) * 32 * KBh;
-    const i32x4 rsc = make_rsrc(a.hs, (uint32_t)hs_bytes);
-    const uint32_t zero = uni(0u);
+    const rsrc_t rsc = store_rsrc(a.hs, (uint32_t)hs_bytes);
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
         const int row = wm * 128 + i * 32 + r32;
@@ -604,7 +613,7 @@ __device__ __forceinline__ void epilogue_swiglu(const GemmArgs& a, const Tile& T
                 int c = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
                 c = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], c, true);
                 const uint32_t off = row < T.rows ? (uint32_t)((int64_t)row * I + hcol + 8 * q) : 0xFFFFFFF0u;
-                bstore4(rq, off, zero, (uint32_t)c);
+                bstore4(rq, off, (uint32_t)c);
             }
             // scale byte of (grow, block (hcol0 + wn 64 + 32 jj) / 32), from lanes 0-31
             const int64_t b = (hcol0 + wn * 64 + jj * 32) / 32;
@@ -612,7 +621,7 @@ __device__ __forceinline__ void epilogue_swiglu(const GemmArgs& a, const Tile& T
                                       ? (uint32_t)((grow >> 5) * 32 * KBh + (b >> 3) * 256 +
                                                    unit_byte((uint32_t)(grow & 31), (uint32_t)(b & 7)))
                                       : 0xFFFFFFF0u;
-            bstore1(rsc, soff, zero, S);
+            bstore1(rsc, soff, S);
         }
     }
 }
