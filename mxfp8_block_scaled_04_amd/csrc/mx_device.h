@@ -111,6 +111,13 @@ __device__ __forceinline__ uint2 quant8(uint4 d, uint32_t S) {
     return r;
 }
 
+// Group offset g clamped to [0, M] (malformed offsets cannot index out of
+// bounds).
+__device__ __forceinline__ int32_t clamp_off(const int32_t* off, int g, int64_t M) {
+    int64_t v = off[g];
+    return (int32_t)(v < 0 ? 0 : (v > M ? M : v));
+}
+
 // Byte position of the scale of (row r mod 32, block b mod 8) inside one
 // 256-byte packed unit: lane register 32*(b%2) + r%32, byte (b%8)/2.
 __device__ __forceinline__ uint32_t unit_byte(uint32_t r32, uint32_t b8) {

@@ -13,6 +13,11 @@ constexpr int kQuantRowsThreads = 512;
 hipError_t launch_quantize_rows(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                                 uint8_t* s, hipStream_t stream);
 
+// P[0..G] (padded column offsets of the column-wise layout) from the group
+// offsets, one workgroup.
+hipError_t launch_cols_prefix(const int32_t* group_offsets, int32_t G, int64_t M, int32_t* padded_offsets,
+                              hipStream_t stream);
+
 hipError_t launch_quantize_cols(const uint16_t* x, int64_t M, int64_t N, int64_t ldx,
                                 const int32_t* group_offsets, int32_t G, uint8_t* qT, uint8_t* sT,
                                 int64_t Mcap, int32_t* padded_offsets, hipStream_t stream);

@@ -1,5 +1,6 @@
 // MXFP8 quantization kernels for gfx950: row-wise (scales along K) and
-// column-wise / transposed (scales along M, per-group block restart).
+// column-wise / transposed (scales along M, per-group block restart).  The
+// dual-layout kernel (both results from one read) is in quantize_dual.hip.
 //
 // Method (lpnh.cn 2479732 section 1; aigc.bar "秘密武器"): one E8M0 scale per
 // 32-element block, the block divided by it and cast to FP8 E4M3; the
@@ -80,11 +81,6 @@ hipError_t launch_quantize_rows(const uint16_t* x, int64_t M, int64_t K, int64_t
 // columns [P[g], P[g+1]) of the transposed result, P[g+1] - P[g] =
 // 256 * ceil(m_g / 256).
 // ---------------------------------------------------------------------------
-
-__device__ __forceinline__ int32_t clamp_off(const int32_t* off, int g, int64_t M) {
-    int64_t v = off[g];
-    return (int32_t)(v < 0 ? 0 : (v > M ? M : v));
-}
 
 // One workgroup of 1024 threads: P[0..G] from the group offsets.
 static_assert(kMaxGroups <= 4 * 1024, "prefix kernel covers 4 groups per thread");
@@ -232,186 +228,17 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(const uint1
     }
 }
 
-// ---------------------------------------------------------------------------
-// Dual layout: one read of x, the row-wise and the column-wise results.  One
-// 256-thread workgroup per padded row tile pt (256 rows of one group, as in
-// the column-wise kernel) and 256-column chunk ct, walked as 4 sub-tiles of
-// 64 columns:
-//  * row-wise: in the load phase, the 4 lanes of a DPP quad hold one
-//    32-column block of each of their two rows; quad max, codes stored 8
-//    bytes per lane to the row-major result, those of sub-tiles 2p and
-//    2p + 1 together (128 contiguous bytes per row, in two store
-//    instructions of 64 bytes per row: ordinary stores, so that L2 joins the
-//    halves of each line -- measured 7 % faster than non-temporal stores on
-//    [131072, 7168] and 19 % on a 16-group [32768, 7168]), scale bytes collected
-//    in LDS in packed dword order (the chunk's 8 blocks of a row are two
-//    dwords) and written once per row at the end, 128 contiguous bytes per
-//    32 rows;
-//  * column-wise: the rows are paired into the transposed LDS tile and
-//    quantized exactly as in the column-wise kernel;
-//  * the loads of the next sub-tile are issued before the column-wise phase
-//    of the current one.
-// Every row of a group lies in exactly one row tile; rows in
-// [M, 32 ceil(M / 32)) get zero row-wise scale bytes, and blocks past N read
-// as zeros, so both packed arrays equal those of the separate kernels.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void quantize_dual_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t N,
-                                                            int64_t ldx, const int32_t* __restrict__ off,
-                                                            const int32_t* __restrict__ P, int32_t G,
-                                                            uint8_t* __restrict__ q, uint8_t* __restrict__ s,
-                                                            uint8_t* __restrict__ qT, uint8_t* __restrict__ sT,
-                                                            int64_t Mcap) {
-    __shared__ uint4 tile[64 * 32];
-    __shared__ uint32_t unit_s[2][64];
-    __shared__ uint32_t row_s[256][2];  // per tile row: packed dwords of K halves 0 and 1 of the chunk
-    __shared__ int32_t sh_g;
-    const int t = threadIdx.x;
-    // column chunks vary fastest: the workgroups in flight read whole rows
-    // (measured 5 % faster than row tiles fastest)
-    const int64_t pt = blockIdx.y;
-    const int64_t ct = blockIdx.x;
-    const int64_t col0 = pt * 256;
-
-    row_s[t][0] = 0;
-    row_s[t][1] = 0;
-    if (t == 0) sh_g = -1;
-    __syncthreads();
-    if (off == nullptr) {
-        if (col0 < ((M + 255) / 256) * 256 && t == 0) sh_g = 0;
-    } else {
-        for (int g = t; g < G; g += 256)
-            if (P[g] <= col0 && col0 < P[g + 1]) sh_g = g;
-    }
-    __syncthreads();
-    const int g = sh_g;
-    int64_t row_begin = 0, row_end = 0;
-    if (g >= 0) {
-        if (off == nullptr) {
-            row_begin = col0;
-            row_end = M;
-        } else {
-            const int64_t o0 = clamp_off(off, g, M), o1 = clamp_off(off, g + 1, M);
-            row_begin = o0 + (col0 - P[g]);
-            row_end = o1;
-        }
-    }
-    const int c8 = t & 7;  // 16-byte column chunk (8 columns) of a sub-tile
-    uint4 da[4], db[4];
-    auto load = [&](int st) {
-        const int64_t ncol = (ct * 4 + st) * 64 + c8 * 8;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int pr = i * 32 + (t >> 3);
-            const int64_t r0 = row_begin + 2 * pr, r1 = r0 + 1;
-            da[i] = make_uint4(0, 0, 0, 0);
-            db[i] = make_uint4(0, 0, 0, 0);
-            if (g >= 0 && ncol < N) {
-                if (r0 < row_end) da[i] = load_stream16(x + r0 * ldx + ncol);
-                if (r1 < row_end) db[i] = load_stream16(x + r1 * ldx + ncol);
-            }
-        }
-    };
-    load(0);
-    // row-wise codes of an even sub-tile wait in registers and go out next to
-    // the odd sub-tile's, so each row gets 128 contiguous bytes at once
-    uint2 pend[4][2];
-    uint8_t* rs = reinterpret_cast<uint8_t*>(row_s);
-    uint8_t* us = reinterpret_cast<uint8_t*>(unit_s);
-#pragma unroll 1
-    for (int st = 0; st < 4; ++st) {
-        const int64_t nt = ct * 4 + st;
-        const int64_t ncol = nt * 64 + c8 * 8;
-        const int b = st * 2 + (c8 >> 2);  // block of the chunk, 0..7
-        // ---- row-wise, from the registers
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int pr = i * 32 + (t >> 3);
-            const int64_t r0 = row_begin + 2 * pr, r1 = r0 + 1;
-            const uint32_t Sa = scale_from_maxmag(quad_max_u32(max_mag8(da[i])));
-            const uint32_t Sb = scale_from_maxmag(quad_max_u32(max_mag8(db[i])));
-            const uint2 ca = quant8(da[i], Sa), cb = quant8(db[i], Sb);
-            if (st & 1) {
-                const int64_t pcol = ncol - 64;
-                if (g >= 0 && pcol < N) {
-                    if (r0 < row_end) store8(q + r0 * N + pcol, pend[i][0]);
-                    if (r1 < row_end) store8(q + r1 * N + pcol, pend[i][1]);
-                }
-                if (g >= 0 && ncol < N) {
-                    if (r0 < row_end) store8(q + r0 * N + ncol, ca);
-                    if (r1 < row_end) store8(q + r1 * N + ncol, cb);
-                }
-            } else {
-                pend[i][0] = ca;
-                pend[i][1] = cb;
-            }
-            if ((t & 3) == 0) {
-                rs[(2 * pr) * 8 + (b & 1) * 4 + (b >> 1)] = (uint8_t)Sa;
-                rs[(2 * pr + 1) * 8 + (b & 1) * 4 + (b >> 1)] = (uint8_t)Sb;
-            }
-        }
-        // ---- pair rows into the transposed tile
-        uint32_t* tw = reinterpret_cast<uint32_t*>(tile);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int pr = i * 32 + (t >> 3);
-            const uint32_t aw[4] = {da[i].x, da[i].y, da[i].z, da[i].w};
-            const uint32_t bw[4] = {db[i].x, db[i].y, db[i].z, db[i].w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t lo = __builtin_amdgcn_perm(bw[k], aw[k], 0x05040100u);
-                const uint32_t hi = __builtin_amdgcn_perm(bw[k], aw[k], 0x07060302u);
-                const int n0 = c8 * 8 + 2 * k, n1 = n0 + 1;
-                tw[n0 * 128 + (((pr >> 2) ^ ((n0 >> 3) & 7)) << 2) + (pr & 3)] = lo;
-                tw[n1 * 128 + (((pr >> 2) ^ ((n1 >> 3) & 7)) << 2) + (pr & 3)] = hi;
-            }
-        }
-        __syncthreads();
-        if (st < 3) load(st + 1);
-        // ---- column-wise from the tile: 8 consecutive rows of one column per task
-        const int j = t & 31;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int n = i * 8 + (t >> 5);
-            const uint4 d = tile[n * 32 + (j ^ ((n >> 3) & 7))];
-            const uint32_t S = scale_from_maxmag(quad_max_u32(max_mag8(d)));
-            const uint2 c = quant8(d, S);
-            const int64_t ng = nt * 64 + n;
-            if (ng < N) store_stream8(qT + ng * Mcap + col0 + 8 * j, c);
-            if ((t & 3) == 0) us[(n >> 5) * 256 + unit_byte((uint32_t)(n & 31), (uint32_t)(j >> 2))] = (uint8_t)S;
-        }
-        __syncthreads();
-        if (t < 128) {
-            const int u = t >> 6;
-            const int64_t rowunit = nt * 2 + u;
-            if (rowunit * 32 < N) {
-                const int64_t KB = Mcap / 32;
-                __builtin_nontemporal_store(unit_s[u][t & 63],
-                                            reinterpret_cast<uint32_t*>(sT + rowunit * 32 * KB + pt * 256) + (t & 63));
-            }
-        }
-    }
-    __syncthreads();
-    // ---- row-wise packed scales: one tile row per thread, two dwords
-    if (g >= 0) {
-        const int64_t r = row_begin + t;
-        const int64_t Mpad = ((M + 31) / 32) * 32;
-        const bool valid = r < row_end, pad = r >= M && r < Mpad;
-        if (valid || pad) {
-            const int64_t KBr = 8 * ((N + 255) / 256);
-            uint32_t* dst = reinterpret_cast<uint32_t*>(s + (r >> 5) * 32 * KBr + ct * 256) + (r & 31);
-            dst[0] = valid ? row_s[t][0] : 0u;
-            dst[32] = valid ? row_s[t][1] : 0u;
-        }
-    }
+hipError_t launch_cols_prefix(const int32_t* group_offsets, int32_t G, int64_t M, int32_t* padded_offsets,
+                              hipStream_t stream) {
+    hipLaunchKernelGGL(cols_prefix_kernel, dim3(1), dim3(1024), 0, stream, group_offsets, G, M, padded_offsets);
+    return hipGetLastError();
 }
 
 hipError_t launch_quantize_cols(const uint16_t* x, int64_t M, int64_t N, int64_t ldx,
                                 const int32_t* group_offsets, int32_t G, uint8_t* qT, uint8_t* sT,
                                 int64_t Mcap, int32_t* padded_offsets, hipStream_t stream) {
     if (group_offsets != nullptr) {
-        hipLaunchKernelGGL(cols_prefix_kernel, dim3(1), dim3(1024), 0, stream, group_offsets, G, M,
-                           padded_offsets);
-        hipError_t e = hipGetLastError();
+        hipError_t e = launch_cols_prefix(group_offsets, G, M, padded_offsets, stream);
         if (e != hipSuccess) return e;
     } else {
         G = 1;
@@ -425,24 +252,6 @@ hipError_t launch_quantize_cols(const uint16_t* x, int64_t M, int64_t N, int64_t
     else
         hipLaunchKernelGGL(quantize_cols_kernel<256>, grid, dim3(256), 0, stream, x, M, N, ldx, group_offsets,
                            (const int32_t*)padded_offsets, G, qT, sT, Mcap);
-    return hipGetLastError();
-}
-
-hipError_t launch_quantize_dual(const uint16_t* x, int64_t M, int64_t N, int64_t ldx,
-                                const int32_t* group_offsets, int32_t G, uint8_t* q, uint8_t* s, uint8_t* qT,
-                                uint8_t* sT, int64_t Mcap, int32_t* padded_offsets, hipStream_t stream) {
-    if (group_offsets != nullptr) {
-        hipLaunchKernelGGL(cols_prefix_kernel, dim3(1), dim3(1024), 0, stream, group_offsets, G, M,
-                           padded_offsets);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    } else {
-        G = 1;
-    }
-    if (N == 0 || Mcap == 0) return hipSuccess;
-    dim3 grid((unsigned)((N + 255) / 256), (unsigned)(Mcap / 256));
-    hipLaunchKernelGGL(quantize_dual_kernel, grid, dim3(256), 0, stream, x, M, N, ldx, group_offsets,
-                       (const int32_t*)padded_offsets, G, q, s, qT, sT, Mcap);
     return hipGetLastError();
 }
 

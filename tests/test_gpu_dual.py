@@ -22,11 +22,18 @@ def _gpu():
     mx.load()
 
 
+FILL = 0xEE  # every output byte is prefilled: the kernel must write all of them
+
+
 def check_dual(x_dev, sizes):
     M, N = x_dev.shape
     off = None if sizes is None else W.offsets_from_sizes(sizes)
     off_dev = None if off is None else torch.from_numpy(off).to(DEV)
-    q, s, qT, sT, P = mx.mx_quantize_dual(x_dev, off_dev)
+    G = 1 if off is None else len(off) - 1
+    Mcap = mx.mx_cols_capacity(M, G)
+    fill = lambda *shape: torch.full(shape, FILL, dtype=torch.uint8, device=DEV)
+    q, s, qT, sT, P = mx.mx_quantize_dual(x_dev, off_dev, Mcap, fill(M, N), fill(mx.mx_scale_bytes(M, N)),
+                                          fill(N, Mcap), fill(mx.mx_scale_bytes(N, Mcap)))
     torch.cuda.synchronize()
     xb = bits(x_dev)
     q_ref, s_ref = oracle.quantize_rows(xb)
@@ -42,7 +49,10 @@ def check_dual(x_dev, sizes):
 
 
 @pytest.mark.parametrize("sizes,N", [([160, 0, 96, 256], 64), ([1, 31, 33, 0, 257, 5], 96), ([300], 288),
-                                     ([0, 0, 64], 32), ([512], 512), ([45], 256), ([7, 250, 700], 160)])
+                                     ([0, 0, 64], 32), ([512], 512), ([45], 256), ([7, 250, 700], 160),
+                                     # the last group's last row tile ends before the packed array's pad
+                                     # rows [M, 32 ceil(M / 32)): they are still written as zeros
+                                     ([5, 256], 64), ([10, 250], 96)])
 def test_dual_groups(sizes, N):
     g = torch.Generator(device=DEV)
     g.manual_seed(sum(sizes) * 7 + N)
