@@ -145,8 +145,9 @@ mx_status mx_quantize_dual(const uint16_t* x, int64_t M, int64_t N, int64_t ldx,
  *   Xq  uint8 [M][K], Xs packed scales (R = M, contraction K)
  *   Wq  uint8 [G][N][K], Ws packed scales of the [G*N][K] matrix
  *   out bf16 [M][N]
- * Requires K % 256 == 0 (MX_ERR_UNSUPPORTED otherwise), 1 <= G <= 4096,
- * 16-byte aligned pointers.  G = 1 with offsets {0, M} is a dense GEMM.
+ * Requires K % 256 == 0 and K > 0 (MX_ERR_UNSUPPORTED otherwise; an empty
+ * contraction is not supported), 1 <= G <= 4096, 16-byte aligned pointers.
+ * G = 1 with offsets {0, M} is a dense GEMM.
  */
 mx_status mx_grouped_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq,
                           const uint8_t* Ws, const int32_t* group_offsets, int32_t G, int64_t M,
@@ -177,7 +178,7 @@ mx_status mx_grouped_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* W
  *           needs them; 16-byte aligned
  * Rows of a group are written once; rows outside every group, and the
  * scale bytes of the padding rows [M, 32 ceil(M / 32)), are left untouched
- * (no output row reads them).  Requires K % 256 == 0 and I % 128 == 0
+ * (no output row reads them).  Requires K % 256 == 0, K > 0 and I % 128 == 0
  * (MX_ERR_UNSUPPORTED otherwise), 1 <= G <= 4096, 16-byte aligned pointers.
  */
 mx_status mx_grouped_gemm_swiglu(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq,
@@ -197,8 +198,9 @@ mx_status mx_grouped_gemm_swiglu(const uint8_t* Xq, const uint8_t* Xs, const uin
  *   dYq uint8 [M][K], dYs packed scales (R = M, contraction K)
  *   WTq uint8 [N][Wcap], WTs packed scales (R = N, contraction Wcap)
  *   dX  bf16 [M][N]
- * Requires K % 256 == 0 (so that expert g starts at column g K), Wcap %
- * 256 == 0, Wcap >= G * K, 1 <= G <= 4096.
+ * Requires K % 256 == 0 and K > 0 (so that expert g starts at column g K;
+ * MX_ERR_UNSUPPORTED otherwise), Wcap % 256 == 0, Wcap >= G * K,
+ * 1 <= G <= 4096.
  */
 mx_status mx_grouped_gemm_dgrad(const uint8_t* dYq, const uint8_t* dYs, const uint8_t* WTq,
                                 const uint8_t* WTs, const int32_t* group_offsets, int32_t G,

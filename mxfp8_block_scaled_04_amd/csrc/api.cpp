@@ -103,7 +103,8 @@ mx_status mx_grouped_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* W
                           void* stream) {
     if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return MX_ERR_SHAPE;
     if (G < 1 || G > kMaxGroups) return MX_ERR_SHAPE;
-    if (K % 256 != 0) return MX_ERR_UNSUPPORTED;
+    // the kernels need at least one 256-wide contraction chunk per tile
+    if (K % 256 != 0 || K == 0) return MX_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return MX_OK;
     if (!Xq || !Xs || !Wq || !Ws || !group_offsets || !out) return MX_ERR_NULL;
     if (!aligned16(Xq) || !aligned16(Xs) || !aligned16(Wq) || !aligned16(Ws) || !aligned16(out))
@@ -122,7 +123,7 @@ mx_status mx_grouped_gemm_swiglu(const uint8_t* Xq, const uint8_t* Xs, const uin
                                  uint8_t* hq, uint8_t* hs, uint16_t* preact, void* stream) {
     if (M < 0 || I < 0 || K < 0 || K % 32 != 0) return MX_ERR_SHAPE;
     if (G < 1 || G > kMaxGroups) return MX_ERR_SHAPE;
-    if (K % 256 != 0 || I % 128 != 0) return MX_ERR_UNSUPPORTED;
+    if (K % 256 != 0 || K == 0 || I % 128 != 0) return MX_ERR_UNSUPPORTED;
     if (M == 0 || I == 0) return MX_OK;
     if (!Xq || !Xs || !Wq || !Ws || !group_offsets || !hq || !hs) return MX_ERR_NULL;
     if (!aligned16(Xq) || !aligned16(Xs) || !aligned16(Wq) || !aligned16(Ws) || !aligned16(hq) || !aligned16(hs) ||
@@ -141,7 +142,7 @@ mx_status mx_grouped_gemm_dgrad(const uint8_t* dYq, const uint8_t* dYs, const ui
                                 int64_t Wcap, uint16_t* dX, void* stream) {
     if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || Wcap < 0) return MX_ERR_SHAPE;
     if (G < 1 || G > kMaxGroups) return MX_ERR_SHAPE;
-    if (K % 256 != 0) return MX_ERR_UNSUPPORTED;
+    if (K % 256 != 0 || K == 0) return MX_ERR_UNSUPPORTED;
     if (Wcap % 256 != 0 || Wcap < (int64_t)G * K) return MX_ERR_CAPACITY;
     if (M == 0 || N == 0) return MX_OK;
     if (!dYq || !dYs || !WTq || !WTs || !group_offsets || !dX) return MX_ERR_NULL;

@@ -11,6 +11,12 @@ import mxfp8_block_scaled_04_amd as mx
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "libmxmoe.h")
 
+# tests/test_sanitize.py runs this module against a sanitizer build of the
+# C-ABI layer (kernel launchers stubbed out) named by MXMOE_ABI_LIB
+if os.environ.get("MXMOE_ABI_LIB"):
+    mx.LIB_PATH = os.environ["MXMOE_ABI_LIB"]
+    mx._lib = None
+
 
 def header_functions():
     src = open(HEADER).read()
@@ -101,6 +107,8 @@ def test_grouped_gemm_validation():
     assert f(FAKE, FAKE, FAKE, FAKE, None, 4, 512, 128, 256, FAKE, None) == 1  # NULL offsets
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 128, 256, P(0x100002), None) == 3  # misaligned out
     assert f(None, None, None, None, None, 4, 0, 128, 256, None, None) == 0    # M == 0: no work
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 128, 0, FAKE, None) == 5    # K == 0: empty contraction
+    assert f(None, None, None, None, None, 4, 0, 128, 0, None, None) == 5      # K == 0 even with no rows
 
 
 def test_grouped_gemm_swiglu_validation():
@@ -108,6 +116,7 @@ def test_grouped_gemm_swiglu_validation():
     # (Xq, Xs, Wq, Ws, offsets, G, M, I, K, hq, hs, preact, stream)
     F5 = (FAKE,) * 5
     assert f(*F5, 4, 512, 2048, 288, FAKE, FAKE, None, None) == 5        # K % 256 != 0
+    assert f(*F5, 4, 512, 2048, 0, FAKE, FAKE, None, None) == 5          # K == 0
     assert f(*F5, 4, 512, 192, 512, FAKE, FAKE, None, None) == 5         # I % 128 != 0
     assert f(*F5, 4, 512, 2048, 250, FAKE, FAKE, None, None) == 2        # K % 32 != 0
     assert f(*F5, 0, 512, 2048, 512, FAKE, FAKE, None, None) == 2        # G < 1
@@ -154,6 +163,7 @@ def test_dgrad_validation():
     f = mx.load().mx_grouped_gemm_dgrad
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 64, 512, 1024, FAKE, None) == 4   # Wcap < G*K
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 64, 288, 2048, FAKE, None) == 5   # K % 256
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 64, 0, 2048, FAKE, None) == 5     # K == 0
     assert f(FAKE, FAKE, FAKE, FAKE, None, 4, 512, 64, 512, 2048, FAKE, None) == 1   # NULL offsets
     assert f(None, None, None, None, None, 4, 0, 64, 512, 2048, None, None) == 0     # M == 0
 
