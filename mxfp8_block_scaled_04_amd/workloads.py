@@ -136,3 +136,41 @@ def moe_ragged(seed=0, device="cuda", M=65536, K=HIDDEN, N=EXPERT_DIM, G=128):
     w = normal_bf16((G, N, K), 0.02, seed + 2, device)
     w_dense = normal_bf16((1, N, K), 0.02, seed + 3, device)
     return dict(x=x, w=w, w_dense=w_dense, sizes=sizes, offsets=offsets_from_sizes(sizes), M=M, N=N, K=K, G=G)
+
+
+# ---------------------------------------------------------------- samples
+
+
+def gemm_sample(M, N, offsets, seed, tile=128, n_random=4096):
+    """Output points of a grouped GEMM [M, N] at which the fp64 oracle is
+    evaluated on the large workloads (parity checks and the CPU-baseline
+    timing share it):
+      * one tile x tile output tile per non-empty group, at a seeded position
+        inside the group (row start a multiple of `tile` from the group's
+        first row, column start a multiple of `tile`), clipped to the group
+        and to N;
+      * n_random seeded uniform (m, n) pairs;
+      * every output element of the groups with fewer than 32 rows;
+      * the last row of every non-empty group at its first and last column.
+    Returns (rows, cols) int64 arrays."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rows = [rng.integers(0, M, n_random)]
+    cols = [rng.integers(0, N, n_random)]
+    G = len(offsets) - 1
+    for g in range(G):
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        if hi <= lo:
+            continue
+        r0 = lo + tile * int(rng.integers(0, -(-(hi - lo) // tile)))
+        c0 = tile * int(rng.integers(0, -(-N // tile)))
+        r = np.arange(r0, min(r0 + tile, hi))
+        c = np.arange(c0, min(c0 + tile, N))
+        rows.append(np.repeat(r, c.size))
+        cols.append(np.tile(c, r.size))
+        if hi - lo < 32:
+            r = np.arange(lo, hi)
+            rows.append(np.repeat(r, N))
+            cols.append(np.tile(np.arange(N), r.size))
+        rows.append(np.array([hi - 1, hi - 1]))
+        cols.append(np.array([0, N - 1]))
+    return np.concatenate(rows).astype(np.int64), np.concatenate(cols).astype(np.int64)

@@ -32,6 +32,7 @@ import mxfp8_block_scaled_04_amd as mx
 import oracle
 from mxfp8_block_scaled_04_amd import workloads as W
 from tests.mxtest import bf16_to_f64, canonical_scales, gemm_tolerance_ok, u8
+from tests.parity import assert_rows_are_oracle, oracle_by_rows, oracle_swiglu_blocks
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -64,10 +65,12 @@ def run_swiglu(x, w, offsets):
     off_dev = torch.from_numpy(offsets).to(DEV)
     mx.mx_grouped_gemm_swiglu(Xq, Xs, Wq.reshape(G, N2, K), Ws, off_dev, hq=hq, hs=hs)
     torch.cuda.synchronize()
+    # the operands are exactly the oracle's quantization of the bf16 inputs;
     # host operands in the oracle's terms: separate gate and up weights
-    hx, hxs = u8(Xq), canonical_scales(Xs, M, K)
-    wq = u8(Wq).reshape(G, I // 32, 2, 32, K)
-    ws = canonical_scales(Ws, G * N2, K).reshape(G, I // 32, 2, 32, K // 32)
+    hx, hxs = assert_rows_are_oracle(x, Xq, Xs)
+    wq, ws = assert_rows_are_oracle(wi.reshape(G * N2, K), Wq, Ws)
+    wq = wq.reshape(G, I // 32, 2, 32, K)
+    ws = ws.reshape(G, I // 32, 2, 32, K // 32)
     Wgq = np.ascontiguousarray(wq[:, :, 0].reshape(G, I, K))
     Wuq = np.ascontiguousarray(wq[:, :, 1].reshape(G, I, K))
     Wgs = np.ascontiguousarray(ws[:, :, 0].reshape(G, I, K // 32))
@@ -88,6 +91,14 @@ def error_radius(h, gate, up, Ag, Au, K):
     return 2.0 * e + 2.0 ** -130
 
 
+def block_scales_of(amax):
+    """The oracle's E8M0 scale byte of blocks whose largest magnitude is each
+    value of amax (a block holding that value and zeros)."""
+    x = np.zeros((np.size(amax), 32), np.float64)
+    x[:, 0] = amax
+    return oracle.quantize_rows_f64(x)[1][:, 0]
+
+
 def check_blocks(q_gpu, s_gpu, h, gate, up, Ag, Au, K, min_exact_codes=0.995, min_exact_scales=0.999):
     """q_gpu [n, 32] codes and s_gpu [n] scale bytes of n blocks against the
     oracle's h, gate, up [n, 32] and abs sums Ag, Au [n, 32]."""
@@ -96,18 +107,23 @@ def check_blocks(q_gpu, s_gpu, h, gate, up, Ag, Au, K, min_exact_codes=0.995, mi
     lo, hi = h - e, h + e
     amax_lo = np.max(np.maximum(np.abs(h) - e, 0.0), axis=1)
     amax_hi = np.max(np.abs(h) + e, axis=1)
-    s_lo = np.array([oracle.block_scale_f64(np.array([a])) for a in amax_lo])
-    s_hi = np.array([oracle.block_scale_f64(np.array([a])) for a in amax_hi])
+    s_lo, s_hi = block_scales_of(amax_lo), block_scales_of(amax_hi)
     bad_s = np.nonzero((s_gpu < s_lo) | (s_gpu > s_hi))[0]
     assert bad_s.size == 0, f"scale outside its interval in block {bad_s[0]}: {s_gpu[bad_s[0]]} not in [{s_lo[bad_s[0]]}, {s_hi[bad_s[0]]}]"
     v = E4M3[q_gpu]
-    for i in range(q_gpu.shape[0]):
-        S = int(s_gpu[i])
-        vlo = E4M3[oracle.quantize_f64_with_scale(lo[i], S)]
-        vhi = E4M3[oracle.quantize_f64_with_scale(hi[i], S)]
-        bad = np.nonzero((v[i] < vlo) | (v[i] > vhi))[0]
-        assert bad.size == 0, (f"block {i} element {bad[0]}: code {q_gpu[i, bad[0]]:#x} outside "
-                               f"[{vlo[bad[0]]}, {vhi[bad[0]]}] for h = {h[i, bad[0]]!r}, S = {S}")
+    # the oracle's encodings of h -/+ e under the kernel's scale byte, one
+    # call per distinct scale byte
+    vlo = np.empty_like(v)
+    vhi = np.empty_like(v)
+    for S in np.unique(s_gpu):
+        sel = s_gpu == S
+        vlo[sel] = E4M3[oracle.quantize_f64_with_scale(lo[sel], int(S))]
+        vhi[sel] = E4M3[oracle.quantize_f64_with_scale(hi[sel], int(S))]
+    bad = np.argwhere((v < vlo) | (v > vhi))
+    if bad.size:
+        i, j = bad[0]
+        raise AssertionError(f"block {i} element {j}: code {q_gpu[i, j]:#x} outside [{vlo[i, j]}, {vhi[i, j]}] "
+                             f"for h = {h[i, j]!r}, S = {s_gpu[i]}")
     h_ref, q_ref, s_ref = oracle.swiglu_quantize(gate, up)
     s_ref = s_ref[:, 0]  # one block per row here
     exact_s = float(np.mean(s_gpu == s_ref))
@@ -123,10 +139,10 @@ def full_check(x, w, sizes):
     I = N2 // 2
     off = W.offsets_from_sizes(sizes)
     hq, hs, ops = run_swiglu(x, w, off)
-    h, q_ref, s_ref, gate, up = oracle.grouped_gemm_swiglu(*ops, off)
     hx, hxs, Wgq, Wgs, Wuq, Wus = ops
-    Ag = oracle.grouped_gemm(abs_codes(hx), hxs, abs_codes(Wgq), Wgs, off)
-    Au = oracle.grouped_gemm(abs_codes(hx), hxs, abs_codes(Wuq), Wus, off)
+    h, q_ref, s_ref, gate, up = oracle_by_rows(oracle.grouped_gemm_swiglu, hx, hxs, ops[2:], off)
+    Ag = oracle_by_rows(oracle.grouped_gemm, abs_codes(hx), hxs, (abs_codes(Wgq), Wgs), off)
+    Au = oracle_by_rows(oracle.grouped_gemm, abs_codes(hx), hxs, (abs_codes(Wuq), Wus), off)
     q = u8(hq)
     hs_h = u8(hs)
     Mpad = 32 * ((M + 31) // 32)
@@ -155,6 +171,18 @@ def test_swiglu_full(sizes, I, K):
     M, G = sum(sizes), len(sizes)
     x = W.normal_bf16((M, K), 1.0, 100 + M, DEV)
     w = W.normal_bf16((G, 2 * I, K), 1.2 / np.sqrt(K), 200 + K, DEV)
+    full_check(x, w, sizes)
+
+
+def test_swiglu_multi_tile_full():
+    """16384 rows, I = 1024 (2048 gate/up columns), K = 256, 16 Dirichlet(0.5)
+    groups: every code and scale byte, each workgroup running >= 2 tiles
+    (>= 512 tiles of 256 x 256 on 256 workgroups)."""
+    M, I, K, G = 16384, 1024, 256, 16
+    sizes = list(W.dirichlet_sizes(M, G, 0.5, 10))
+    assert sum(-(-int(m) // 256) for m in sizes) * (2 * I // 256) >= 512
+    x = W.normal_bf16((M, K), 1.0, 47, DEV)
+    w = W.normal_bf16((G, 2 * I, K), 1.2 / np.sqrt(K), 48, DEV)
     full_check(x, w, sizes)
 
 
@@ -193,22 +221,34 @@ def test_swiglu_gate_up_sampled():
     I = d["N"] // 2
     off = d["offsets"]
     hq, hs, ops = run_swiglu(d["x"], d["w"], off)
+    # the recipe's sample in 32-wide blocks of h: a 128-row x 4-block (128 x
+    # 128) tile per non-empty group, 4096 uniform blocks, every block of the
+    # groups below 32 rows, the first and last block of each group's last row
     rng = np.random.default_rng(5)
-    rows = list(rng.integers(0, M, 384))
-    blocks = list(rng.integers(0, I // 32, 384))
+    nb = I // 32
+    rows = [rng.integers(0, M, 4096)]
+    blocks = [rng.integers(0, nb, 4096)]
     for g in range(G):
         lo, hi = int(off[g]), int(off[g + 1])
-        if hi > lo:
-            for r in (lo, hi - 1):
-                rows += [r, r]
-                blocks += [0, I // 32 - 1]
-    rows = np.array(rows, np.int64)
-    blocks = np.array(blocks, np.int64)
-    h, q_ref, s_ref, gate, up = oracle.grouped_gemm_swiglu_blocks(*ops, off, rows, blocks)
+        if hi <= lo:
+            continue
+        r0 = lo + 128 * int(rng.integers(0, -(-(hi - lo) // 128)))
+        b0 = 4 * int(rng.integers(0, nb // 4))
+        r = np.arange(r0, min(r0 + 128, hi))
+        rows.append(np.repeat(r, 4))
+        blocks.append(np.tile(np.arange(b0, b0 + 4), r.size))
+        if hi - lo < 32:
+            rows.append(np.repeat(np.arange(lo, hi), nb))
+            blocks.append(np.tile(np.arange(nb), hi - lo))
+        rows.append(np.array([hi - 1, hi - 1]))
+        blocks.append(np.array([0, nb - 1]))
+    rows = np.concatenate(rows).astype(np.int64)
+    blocks = np.concatenate(blocks).astype(np.int64)
+    h, q_ref, s_ref, gate, up = oracle_swiglu_blocks(*ops, off, rows, blocks)
     hx, hxs, Wgq, Wgs, Wuq, Wus = ops
     # sums of |x| |w|: the same blocks over the magnitudes of the codes
-    _, _, _, Ag, Au = oracle.grouped_gemm_swiglu_blocks(abs_codes(hx), hxs, abs_codes(Wgq), Wgs, abs_codes(Wuq), Wus,
-                                                        off, rows, blocks)
+    _, _, _, Ag, Au = oracle_swiglu_blocks(abs_codes(hx), hxs, abs_codes(Wgq), Wgs, abs_codes(Wuq), Wus,
+                                           off, rows, blocks)
     q = u8(hq)
     s = oracle.unpack_scales(u8(hs), M, I)
     cols = blocks[:, None] * 32 + np.arange(32)[None, :]
