@@ -51,6 +51,14 @@ def quant_bytes(M, K):
     return 2 * M * K + M * K + M * K // 32
 
 
+# sources each kernel is built from (its .hip file and the headers it includes)
+KERNEL_SOURCES = {
+    "quantize": ("quantize.hip", "mx_device.h", "mx_internal.h"),
+    "quantize_dual": ("quantize_dual.hip", "mx_device.h", "mx_internal.h"),
+    "grouped_gemm": ("grouped_gemm.hip", "mx_device.h", "mx_internal.h"),
+}
+
+
 def source_digest(*names):
     h = hashlib.sha256()
     for n in names:
@@ -59,10 +67,10 @@ def source_digest(*names):
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel, digest):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 --pmc
-    summary (profiles/<kernel>_pmc.txt), if it was taken on this source."""
-    path = os.path.join(ROOT, "profiles", kernel + "_pmc.txt")
+def read_profile(name, digest):
+    """key: value lines of the committed rocprofv3 summary profiles/<name>.txt,
+    or None when it is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", name + ".txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -73,8 +81,12 @@ def load_traffic(kernel, digest):
                 vals[k.strip()] = v.strip()
     if vals.get("source_sha256") != digest:
         return None
+    return vals
+
+
+def profile_float(vals, key):
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals[key]) if vals is not None else None
     except (KeyError, ValueError):
         return None
 
@@ -96,43 +108,64 @@ class Timer:
         return self.a.elapsed_time(self.b) / steps  # ms per launch
 
 
-def cpu_baseline(x_cpu_rows, seed):
-    """Oracle (as it stands) on a bounded sample: rows then cols of the given
-    bf16 rows, split over host threads (ctypes releases the GIL)."""
-    import numpy as np
-    import oracle
-
+def host_threads():
+    """Host threads the oracle may use: the CPUs this process may run on,
+    at most 16 (the GPU machine's CPU share per GPU)."""
     try:
-        cores = len(os.sched_getaffinity(0))
+        visible = len(os.sched_getaffinity(0))
     except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = max(1, min(cores, 16))
-    bits = x_cpu_rows
-    M, K = bits.shape
-    chunks = np.array_split(np.arange(M), cores)
+        visible = os.cpu_count() or 1
+    return max(1, min(visible, 16)), visible
+
+
+def oracle_quantize_pass(oracle, bits, threads):
+    """The oracle (as it stands) on bf16 bits [M, K]: the row-wise pass, then
+    the column-wise pass (one group; 256-row slabs are independent), each
+    split over `threads` host threads (ctypes releases the GIL).  Returns the
+    wall time of each pass."""
+    import numpy as np
+
+    M = bits.shape[0]
+    chunks = [c for c in np.array_split(np.arange(M), threads) if c.size]
     t0 = time.perf_counter()
-    with concurrent.futures.ThreadPoolExecutor(cores) as ex:
+    with concurrent.futures.ThreadPoolExecutor(threads) as ex:
         list(ex.map(lambda r: oracle.quantize_rows(bits[r[0]:r[-1] + 1]), chunks))
     t_rows = time.perf_counter() - t0
-    # column-wise: blocks of 32 rows; 256-row slabs are independent
-    slabs = [np.arange(i, min(i + 256, M)) for i in range(0, M, 256)]
-    groups = np.array_split(np.arange(len(slabs)), cores)
+    slabs = [(i, min(i + 256, M)) for i in range(0, M, 256)]
+    groups = [g for g in np.array_split(np.arange(len(slabs)), threads) if g.size]
 
     def run_cols(gi):
         for i in gi:
-            r = slabs[i]
-            oracle.quantize_cols(bits[r[0]:r[-1] + 1])
+            a, b = slabs[i]
+            oracle.quantize_cols(bits[a:b])
 
     t0 = time.perf_counter()
-    with concurrent.futures.ThreadPoolExecutor(cores) as ex:
+    with concurrent.futures.ThreadPoolExecutor(threads) as ex:
         list(ex.map(run_cols, groups))
-    t_cols = time.perf_counter() - t0
+    return t_rows, time.perf_counter() - t0
+
+
+def cpu_baseline(x_bits, seed, one_thread_rows):
+    """The CPU oracle on the whole quantize workload (row-wise then
+    column-wise pass) over the host threads, plus the same on one thread
+    over its first `one_thread_rows` rows; both as algorithmic TB/s."""
+    import oracle
+
+    threads, visible = host_threads()
+    M, K = x_bits.shape
+    t_rows, t_cols = oracle_quantize_pass(oracle, x_bits, threads)
     tbs = 2 * quant_bytes(M, K) / (t_rows + t_cols) / 1e12
-    return {"value": tbs, "unit": "TB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{M} rows x {K} of the quantize workload (seed {seed}), row-wise then column-wise pass; "
+    m1 = min(one_thread_rows, M)
+    t1r, t1c = oracle_quantize_pass(oracle, x_bits[:m1], 1)
+    return {"value": tbs, "unit": "TB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole quantize workload, {M} x {K} bf16 (seed {seed}): row-wise then column-wise "
+                      f"pass on {threads} host threads ({visible} CPUs visible, at most 16 used); "
                       f"{t_rows:.2f} s + {t_cols:.2f} s wall",
-            "gemm_oracle": gemm_oracle_rate(seed, cores),
-            "gemm_oracle_gate_up": gemm_oracle_gate_up_sample(seed, cores)}
+            "one_thread": {"value": 2 * quant_bytes(m1, K) / (t1r + t1c) / 1e12, "unit": "TB/s", "cores": 1,
+                           "sample": f"first {m1} rows x {K}, row-wise then column-wise pass; "
+                                     f"{t1r:.2f} s + {t1c:.2f} s wall"},
+            "gemm_oracle": gemm_oracle_rate(seed, threads),
+            "gemm_oracle_gate_up": gemm_oracle_gate_up_sample(seed, threads)}
 
 
 def gemm_oracle_rate(seed, cores):
@@ -195,17 +228,7 @@ def gemm_oracle_gate_up_sample(seed, cores, device="cuda"):
     Wq, Ws = quant_all(wb)
     del wb
     Wq, Ws = Wq.reshape(G, N, K), Ws.reshape(G, N, K // 32)
-    rng = np.random.default_rng(seed)
-    rows = [rng.integers(0, M, 4096)]
-    cols = [rng.integers(0, N, 4096)]
-    for g in range(G):
-        lo, hi = int(off[g]), int(off[g + 1])
-        if hi <= lo:
-            continue
-        r = np.arange(lo, min(lo + 128, hi))
-        rows.append(np.repeat(r, 128))
-        cols.append(np.tile(np.arange(128), r.size))
-    rows, cols = np.concatenate(rows).astype(np.int64), np.concatenate(cols).astype(np.int64)
+    rows, cols = W.gemm_sample(M, N, off, seed)
     parts = np.array_split(np.arange(rows.size), cores)
     t0 = time.perf_counter()
     with concurrent.futures.ThreadPoolExecutor(cores) as ex:
@@ -214,8 +237,9 @@ def gemm_oracle_gate_up_sample(seed, cores, device="cuda"):
     rate = 2.0 * rows.size * K / t
     return {"gflops": rate / 1e9, "s": t, "cores": cores, "points": int(rows.size),
             "extrapolated_full_s": 2.0 * M * N * K / rate,
-            "sample": f"gate+up workload {M} x {N} x {K}, {G} experts (seed {seed}): a 128 x 128 patch per "
-                      f"non-empty group + 4096 uniform points; full-size time extrapolated, not measured"}
+            "sample": f"gate+up workload {M} x {N} x {K}, {G} experts (seed {seed}): a 128 x 128 tile per "
+                      f"non-empty group + 4096 uniform points + every element of the groups below 32 rows "
+                      f"(the parity tests' sample); full-size time extrapolated, not measured"}
 
 
 def launch_stats(torch, fn, n):
@@ -284,8 +308,7 @@ def bench_quant(torch, mx, W, args):
     }
     sample = None
     if not args.no_cpu:
-        n = args.cpu_rows
-        sample = x[:n].cpu().contiguous().view(torch.int16).numpy().view("uint16")
+        sample = x.cpu().contiguous().view(torch.int16).numpy().view("uint16")
     del x, q, s, qT, sT
     torch.cuda.empty_cache()
     return res, sample
@@ -396,29 +419,6 @@ def bench_gemm(torch, mx, W, args):
     return out
 
 
-def bench_vendor(torch, W, args):
-    """The vendor library's block-scaled GEMM on the ragged case's dense twin
-    (65536 x 2048 x 7168, E4M3 with E8M0 scales per 32 of K, bf16 out) through
-    torch._scaled_mm, for context.  Operands are seeded random codes with unit
-    scales: the timing does not depend on the values."""
-    g = torch.Generator(device="cuda")
-    g.manual_seed(args.seed)
-    M, N, K = 65536, 2048, 7168
-    a = torch.randn((M, K), device="cuda", generator=g).mul_(0.5).to(torch.float8_e4m3fn)
-    b = torch.randn((N, K), device="cuda", generator=g).mul_(0.5).to(torch.float8_e4m3fn)
-    sa = torch.full((M, K // 32), 127, dtype=torch.uint8, device="cuda").view(torch.float8_e8m0fnu)
-    sb = torch.full((N, K // 32), 127, dtype=torch.uint8, device="cuda").view(torch.float8_e8m0fnu)
-    fn = lambda: torch._scaled_mm(a, b.t(), sa, sb, out_dtype=torch.bfloat16)
-    try:
-        for _ in range(args.warmup):
-            fn()
-        torch.cuda.synchronize()
-        ms = Timer(torch).run(fn, args.steps)
-    except Exception as ex:  # the library may lack the block-scaled path
-        return {"error": f"{type(ex).__name__}: {str(ex)[:200]}"}
-    return {"M": M, "N": N, "K": K, "ms": ms, "tflops": tflops(M, N, K, ms), "via": "torch._scaled_mm (hipBLASLt)"}
-
-
 def bench_layer(torch, mx, W, args):
     """One MoE layer's expert computation, forward + backward, on the gate+up /
     down workloads' routing (32768 rows, H 7168, I 2048, 16 experts): per-stage
@@ -486,17 +486,16 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-gemm", action="store_true", help="skip the grouped-GEMM section")
     ap.add_argument("--no-layer", action="store_true", help="skip the MoE-layer chain")
-    ap.add_argument("--vendor-baseline", action="store_true",
-                    help="also time torch._scaled_mm (hipBLASLt) MXFP8 on the dense 65536 x 2048 x 7168 GEMM")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=32768, help="rows of the oracle sample")
+    ap.add_argument("--cpu-rows-1t", type=int, default=8192,
+                    help="rows of the one-thread oracle figure (the threaded figure runs the whole input)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) a few times, "
                          "so that HBM counters can be scaled against a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU layout is described in DESIGN.md", file=sys.stderr)
+              "sharding over several GPUs is a design note, not code", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -516,16 +515,53 @@ def main():
     quant, sample = bench_quant(torch, mx, W, args)
     gemm = None if args.no_gemm else bench_gemm(torch, mx, W, args)
     layer = None if args.no_layer else bench_layer(torch, mx, W, args)
-    vendor = bench_vendor(torch, W, args) if args.vendor_baseline else None
-    cpu = None if sample is None else cpu_baseline(sample, args.seed)
+    cpu = None if sample is None else cpu_baseline(sample, args.seed, args.cpu_rows_1t)
 
     ms_step = quant["ms_rows"] + quant["ms_cols"]
     value = 2 * quant["bytes_per_pass"] / (ms_step * 1e-3) / 1e12
-    dominant = "quantize_cols_kernel" if quant["ms_cols"] >= quant["ms_rows"] else "quantize_rows_kernel"
+    kname = "quantize_cols_kernel" if quant["ms_cols"] >= quant["ms_rows"] else "quantize_rows_kernel"
     dom_ms = max(quant["ms_rows"], quant["ms_cols"])
     achieved = quant["bytes_per_pass"] / (dom_ms * 1e-3) / 1e9  # GB/s
-    digest = source_digest("quantize.hip", "mx_device.h")
-    traffic = load_traffic(dominant, digest)
+    qdigest = source_digest(*KERNEL_SOURCES["quantize"])
+    pmc = read_profile(kname + "_pmc", qdigest)
+    trace = read_profile(kname + "_trace", qdigest)
+    trace_us = profile_float(trace, "avg_us")
+    roofline = {
+        "bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_TBS * 1000, "unit": "GB/s",
+        "frac": achieved / (HBM_PEAK_TBS * 1000), "traffic": profile_float(pmc, "hbm_bytes_per_launch"),
+        "algorithmic_bytes_per_launch": quant["bytes_per_pass"],
+        "timing": "mean launch time from HIP events on the launch stream over the timed launches of this run",
+        "source_sha256": qdigest,
+        # the same quantity from the committed rocprofv3 kernel trace (another
+        # run of this command on these kernel sources; null if they changed)
+        "kernel_trace": None if trace_us is None else {
+            "avg_us": trace_us, "achieved": quant["bytes_per_pass"] / (trace_us * 1e-6) / 1e9,
+            "frac": quant["bytes_per_pass"] / (trace_us * 1e-6) / 1e9 / (HBM_PEAK_TBS * 1000),
+            "file": f"profiles/{kname}_trace.txt"},
+    }
+    roofline_gemm = None
+    if gemm is not None:
+        gu = gemm["gate_up"]
+        flops = 2.0 * gu["M"] * gu["N"] * gu["K"]
+        gdigest = source_digest(*KERNEL_SOURCES["grouped_gemm"])
+        gpmc = read_profile("grouped_gemm_gate_up_pmc", gdigest)
+        gtrace = read_profile("grouped_gemm_gate_up_trace", gdigest)
+        gtrace_us = profile_float(gtrace, "avg_us")
+        roofline_gemm = {
+            "bound": "mfma", "kernel": "grouped_gemm_kernel",
+            "workload": f"gate+up {gu['M']} x {gu['N']} x {gu['K']}, {gu['G']} experts",
+            "achieved": flops / (gu["ms"] * 1e-3) / 1e12, "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": flops / (gu["ms"] * 1e-3) / 1e12 / MFMA_FP8_PEAK_TFLOPS,
+            "traffic": profile_float(gpmc, "hbm_bytes_per_launch"),
+            "algorithmic_flops_per_launch": flops,
+            "mfma_busy": profile_float(gpmc, "mfma_busy"),
+            "timing": "mean launch time from HIP events on the launch stream over the timed launches of this run",
+            "source_sha256": gdigest,
+            "kernel_trace": None if gtrace_us is None else {
+                "avg_us": gtrace_us, "achieved": flops / (gtrace_us * 1e-6) / 1e12,
+                "frac": flops / (gtrace_us * 1e-6) / 1e12 / MFMA_FP8_PEAK_TFLOPS,
+                "file": "profiles/grouped_gemm_gate_up_trace.txt"},
+        }
     line = {
         "metric": METRIC,
         "value": value,
@@ -544,18 +580,14 @@ def main():
                    "tbs_rows": quant["tbs_rows"], "tbs_cols": quant["tbs_cols"],
                    "ms_rows": quant["ms_rows"], "ms_cols": quant["ms_cols"],
                    "launch_ms": quant["launch_ms"], "copy_tbs_measured": quant["copy_tbs"],
-                   "frac_copy_ceiling": value / quant["copy_tbs"],
-                   "source_sha256": digest},
-        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_TBS * 1000,
-                     "unit": "GB/s", "frac": achieved / (HBM_PEAK_TBS * 1000), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": quant["bytes_per_pass"]},
+                   "frac_copy_ceiling": value / quant["copy_tbs"]},
+        "roofline": roofline,
+        "roofline_gemm": roofline_gemm,
         "cpu_baseline": cpu,
         "quantize_dual": dict(quant["dual"], workload="bf16 [131072, 7168] -> row-wise + column-wise MXFP8, one read"),
         "gemm": gemm,
         "moe_layer": layer,
     }
-    if vendor is not None:
-        line["vendor_dense_mxfp8"] = vendor
     print(json.dumps(line), flush=True)
 
 
