@@ -22,9 +22,15 @@ __device__ __forceinline__ uint4 load_stream16(const void* p) {
 __device__ __forceinline__ void store_stream8(void* p, uint2 v) {
     __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(p));
 }
-// Ordinary (cached) 8-byte store: where one store instruction covers only part
-// of each 128-byte line it touches, L2 can merge the parts before write-back.
+// Ordinary (cached) 8- and 16-byte stores: where one store instruction covers
+// only part of each 128-byte line it touches, L2 can merge the parts before
+// write-back.
 __device__ __forceinline__ void store8(void* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }
+__device__ __forceinline__ void store16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+// Streaming (non-temporal) 16-byte store.
+__device__ __forceinline__ void store_stream16(void* p, uint4 v) {
+    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
+}
 
 // Largest group count accepted by the grouped entry points.
 constexpr int kMaxGroups = 4096;

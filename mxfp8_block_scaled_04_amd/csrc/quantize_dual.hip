@@ -17,17 +17,19 @@ namespace mx {
 // the column-wise kernel) and 256-column chunk ct, walked as 4 sub-tiles of
 // 64 columns:
 //  * row-wise: in the load phase, the 4 lanes of a DPP quad hold one
-//    32-column block of each of their two rows; quad max, codes stored 8
-//    bytes per lane to the row-major result, those of sub-tiles 2p and
-//    2p + 1 together (128 contiguous bytes per row, in two store
-//    instructions of 64 bytes per row: ordinary stores, so that L2 joins the
-//    halves of each line -- measured 7 % faster than non-temporal stores on
-//    [131072, 7168] and 19 % on a 16-group [32768, 7168]), scale bytes collected
-//    in LDS in packed dword order (the chunk's 8 blocks of a row are two
-//    dwords) and written once per row at the end, 128 contiguous bytes per
-//    32 rows;
-//  * column-wise: the rows are paired into the transposed LDS tile and
-//    quantized exactly as in the column-wise kernel;
+//    32-column block of each of their two rows; quad max, codes exchanged
+//    between adjacent lanes so that each lane stores 16 bytes of one row,
+//    those of sub-tiles 2p and 2p + 1 together (128 contiguous bytes per
+//    row, in two store instructions of 64 bytes per row: ordinary stores, so
+//    that L2 joins the halves of each line -- measured 7 % faster than
+//    non-temporal stores on [131072, 7168] and 19 % on a 16-group
+//    [32768, 7168]), scale bytes collected in LDS in packed dword order (the
+//    chunk's 8 blocks of a row are two dwords) and written once per row at
+//    the end, 128 contiguous bytes per 32 rows;
+//  * column-wise: the rows are paired into the transposed LDS tile; each
+//    lane quantizes 16 consecutive rows of a column (a lane pair per 32-row
+//    block) with the element map of the column-wise kernel and stores 16
+//    code bytes (16-byte stores: 1-4 % faster than 8-byte ones);
 //  * the loads of the next sub-tile are issued before the column-wise phase
 //    of the current one.
 // Every row of a group lies in exactly one row tile; rows in
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(const uint16_t* __re
     load(0);
     // row-wise codes of an even sub-tile wait in registers and go out next to
     // the odd sub-tile's, so each row gets 128 contiguous bytes at once
-    uint2 pend[4][2];
+    uint4 pend[4];
     uint8_t* rs = reinterpret_cast<uint8_t*>(row_s);
     uint8_t* us = reinterpret_cast<uint8_t*>(unit_s);
 #pragma unroll 1
@@ -109,19 +111,22 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(const uint16_t* __re
             const uint32_t Sa = scale_from_maxmag(quad_max_u32(max_mag8(da[i])));
             const uint32_t Sb = scale_from_maxmag(quad_max_u32(max_mag8(db[i])));
             const uint2 ca = quant8(da[i], Sa), cb = quant8(db[i], Sb);
+            // adjacent lanes (c8 even / odd) swap halves: the even lane then
+            // holds 16 code bytes of row r0 (columns ncol .. ncol + 15), the odd
+            // lane those of row r1 (columns ncol - 8 .. ncol + 7)
+            const uint2 snd = (c8 & 1) ? ca : cb;
+            const uint32_t rx = (uint32_t)__builtin_amdgcn_mov_dpp((int)snd.x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+            const uint32_t ry = (uint32_t)__builtin_amdgcn_mov_dpp((int)snd.y, 0xB1, 0xF, 0xF, false);
+            const uint4 o = (c8 & 1) ? make_uint4(rx, ry, cb.x, cb.y) : make_uint4(ca.x, ca.y, rx, ry);
+            const int64_t rr = (c8 & 1) ? r1 : r0;
+            const int64_t cc = ncol - (c8 & 1) * 8;
             if (st & 1) {
-                const int64_t pcol = ncol - 64;
-                if (g >= 0 && pcol < N) {
-                    if (r0 < row_end) store8(q + r0 * N + pcol, pend[i][0]);
-                    if (r1 < row_end) store8(q + r1 * N + pcol, pend[i][1]);
-                }
-                if (g >= 0 && ncol < N) {
-                    if (r0 < row_end) store8(q + r0 * N + ncol, ca);
-                    if (r1 < row_end) store8(q + r1 * N + ncol, cb);
+                if (g >= 0 && rr < row_end) {
+                    if (cc - 64 < N) store16(q + rr * N + cc - 64, pend[i]);
+                    if (cc < N) store16(q + rr * N + cc, o);
                 }
             } else {
-                pend[i][0] = ca;
-                pend[i][1] = cb;
+                pend[i] = o;
             }
             if ((t & 3) == 0) {
                 rs[(2 * pr) * 8 + (b & 1) * 4 + (b >> 1)] = (uint8_t)Sa;
@@ -146,17 +151,25 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(const uint16_t* __re
         }
         __syncthreads();
         if (st < 3) load(st + 1);
-        // ---- column-wise from the tile: 8 consecutive rows of one column per task
-        const int j = t & 31;
+        // ---- column-wise from the tile: 16 consecutive rows of one column per
+        // task (two 16-byte granules), a 32-row block per lane pair
+        const int jj = t & 15;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int n = i * 8 + (t >> 5);
-            const uint4 d = tile[n * 32 + (j ^ ((n >> 3) & 7))];
-            const uint32_t S = scale_from_maxmag(quad_max_u32(max_mag8(d)));
-            const uint2 c = quant8(d, S);
+        for (int i = 0; i < 4; ++i) {
+            const int n = i * 16 + (t >> 4);
+            const int sw = (n >> 3) & 7;
+            const uint4 d0 = tile[n * 32 + ((2 * jj) ^ sw)];
+            const uint4 d1 = tile[n * 32 + ((2 * jj + 1) ^ sw)];
+            uint32_t m = max_mag8(d0);
+            const uint32_t m1 = max_mag8(d1);
+            m = m > m1 ? m : m1;
+            const uint32_t mo = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false);  // the pair's other lane
+            m = m > mo ? m : mo;
+            const uint32_t S = scale_from_maxmag(m);
+            const uint2 c0 = quant8(d0, S), c1 = quant8(d1, S);
             const int64_t ng = nt * 64 + n;
-            if (ng < N) store_stream8(qT + ng * Mcap + col0 + 8 * j, c);
-            if ((t & 3) == 0) us[(n >> 5) * 256 + unit_byte((uint32_t)(n & 31), (uint32_t)(j >> 2))] = (uint8_t)S;
+            if (ng < N) store_stream16(qT + ng * Mcap + col0 + 16 * jj, make_uint4(c0.x, c0.y, c1.x, c1.y));
+            if ((t & 1) == 0) us[(n >> 5) * 256 + unit_byte((uint32_t)(n & 31), (uint32_t)(jj >> 1))] = (uint8_t)S;
         }
         __syncthreads();
         if (t < 128) {

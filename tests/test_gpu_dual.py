@@ -11,6 +11,7 @@ import mxfp8_block_scaled_04_amd as mx
 import oracle
 from mxfp8_block_scaled_04_amd import workloads as W
 from tests.mxtest import bits, canonical_scales, u8
+from tests.parity import assert_cols_are_oracle, assert_rows_are_oracle
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -25,16 +26,23 @@ def _gpu():
 FILL = 0xEE  # every output byte is prefilled: the kernel must write all of them
 
 
-def check_dual(x_dev, sizes):
+def prefilled_dual(x_dev, off):
+    """mx_quantize_dual into outputs whose every byte starts as FILL."""
     M, N = x_dev.shape
-    off = None if sizes is None else W.offsets_from_sizes(sizes)
     off_dev = None if off is None else torch.from_numpy(off).to(DEV)
     G = 1 if off is None else len(off) - 1
     Mcap = mx.mx_cols_capacity(M, G)
     fill = lambda *shape: torch.full(shape, FILL, dtype=torch.uint8, device=DEV)
-    q, s, qT, sT, P = mx.mx_quantize_dual(x_dev, off_dev, Mcap, fill(M, N), fill(mx.mx_scale_bytes(M, N)),
-                                          fill(N, Mcap), fill(mx.mx_scale_bytes(N, Mcap)))
+    out = mx.mx_quantize_dual(x_dev, off_dev, Mcap, fill(M, N), fill(mx.mx_scale_bytes(M, N)),
+                              fill(N, Mcap), fill(mx.mx_scale_bytes(N, Mcap)))
     torch.cuda.synchronize()
+    return out
+
+
+def check_dual(x_dev, sizes):
+    M, N = x_dev.shape
+    off = None if sizes is None else W.offsets_from_sizes(sizes)
+    q, s, qT, sT, P = prefilled_dual(x_dev, off)
     xb = bits(x_dev)
     q_ref, s_ref = oracle.quantize_rows(xb)
     assert np.array_equal(u8(q), q_ref), np.argwhere(u8(q) != q_ref)[:5]
@@ -74,47 +82,23 @@ def test_dual_empty_rows():
     check_dual(x, [0, 0, 0])
 
 
-def test_dual_down_backward_sampled():
-    # the down projection's gradient dY [32768, 7168] with its 16 groups
+def test_dual_down_backward_full():
+    """The down projection's gradient dY [32768, 7168] with its 16 groups:
+    every row-wise and column-wise code, packed scale byte and padded offset
+    against the oracle."""
     d = W.moe_down_backward(seed=0, device=DEV)
-    off = d["offsets"]
     x = d["dy"]
-    M, N = x.shape
-    q, s, qT, sT, P = mx.mx_quantize_dual(x, torch.from_numpy(off).to(DEV))
+    q, s, qT, sT, P = prefilled_dual(x, d["offsets"])
     torch.cuda.synchronize()
-    rng = np.random.default_rng(3)
-    rows = np.unique(np.concatenate([[0, M - 1], off[1:-1], off[1:-1] - 1, rng.integers(0, M, 64)]))
-    rows = rows[(rows >= 0) & (rows < M)]
-    q_ref, s_ref = oracle.quantize_rows(bits(x[torch.from_numpy(rows).to(DEV)]))
-    assert np.array_equal(u8(q[torch.from_numpy(rows).to(DEV)]), q_ref)
-    assert np.array_equal(canonical_scales(s, M, N)[rows], s_ref)
-    Mcap = qT.shape[1]
-    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 24)]))
-    qT_ref, sT_ref, P_ref = oracle.quantize_cols(bits(x[:, torch.from_numpy(cols).to(DEV)]), off, Mcap)
-    assert np.array_equal(P.cpu().numpy(), P_ref)
-    assert np.array_equal(u8(qT[torch.from_numpy(cols).to(DEV)]), qT_ref)
-    assert np.array_equal(canonical_scales(sT, N, Mcap)[cols], sT_ref)
+    assert_rows_are_oracle(x, q, s)
+    assert_cols_are_oracle(x, d["offsets"], qT, sT, P)
 
 
-def test_dual_quant_bandwidth_sampled():
+def test_dual_quant_bandwidth_full():
     """The quantize-bandwidth workload [131072, 7168] with no groups, as the
-    benchmark runs it: sampled rows of the row-wise result (every 64-column
-    sub-tile pair of each, so both halves of the jointly stored 128-byte
-    pieces) and sampled columns of the column-wise result."""
+    benchmark runs it: both results in full against the oracle."""
     x = W.quant_bandwidth(seed=0, device=DEV)
-    M, N = x.shape
-    q, s, qT, sT, P = mx.mx_quantize_dual(x)
-    torch.cuda.synchronize()
+    q, s, qT, sT, P = prefilled_dual(x, None)
     assert P is None
-    rng = np.random.default_rng(4)
-    rows = np.unique(np.concatenate([[0, 1, 255, 256, M - 1], rng.integers(0, M, 128)]))
-    ridx = torch.from_numpy(rows).to(DEV)
-    q_ref, s_ref = oracle.quantize_rows(bits(x[ridx]))
-    assert np.array_equal(u8(q[ridx]), q_ref)
-    assert np.array_equal(canonical_scales(s, M, N)[rows], s_ref)
-    Mcap = qT.shape[1]
-    cols = np.unique(np.concatenate([[0, 63, 64, 255, 256, N - 1], rng.integers(0, N, 16)]))
-    cidx = torch.from_numpy(cols).to(DEV)
-    qT_ref, sT_ref, _ = oracle.quantize_cols(bits(x[:, cidx]), None, Mcap)
-    assert np.array_equal(u8(qT[cidx]), qT_ref)
-    assert np.array_equal(canonical_scales(sT, N, Mcap)[cols], sT_ref)
+    assert_rows_are_oracle(x, q, s)
+    assert_cols_are_oracle(x, None, qT, sT)

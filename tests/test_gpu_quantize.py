@@ -10,6 +10,7 @@ import mxfp8_block_scaled_04_amd as mx
 import oracle
 from mxfp8_block_scaled_04_amd import workloads as W
 from tests.mxtest import bits, canonical_scales, u8
+from tests.parity import assert_cols_are_oracle, assert_rows_are_oracle
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -86,18 +87,14 @@ def test_rows_element_map_exhaustive():
     assert set(np.unique(s_ref).tolist()) == set(range(0, 247))
 
 
-def test_rows_quant_bandwidth_sampled():
+def test_rows_quant_bandwidth_full():
+    """The quantize-bandwidth workload [131072, 7168] row-wise, as the
+    benchmark runs it: every code and every packed scale byte against the
+    oracle (threaded over row ranges)."""
     x = W.quant_bandwidth(seed=0, device=DEV)
-    M, K = x.shape
     q, s = mx.mx_quantize_rows(x)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([[0, 1, M - 1], rng.integers(0, M, 200)]))
-    xb = bits(x[torch.from_numpy(rows).to(DEV)])
-    q_ref, s_ref = oracle.quantize_rows(xb)
-    assert np.array_equal(u8(q[torch.from_numpy(rows).to(DEV)]), q_ref)
-    s_all = canonical_scales(s, M, K)
-    assert np.array_equal(s_all[rows], s_ref)
+    assert_rows_are_oracle(x, q, s)
 
 
 def check_cols(x_dev, sizes):
@@ -136,43 +133,31 @@ def test_cols_empty_rows():
     check_cols(x, [0, 0, 0])
 
 
-def test_cols_down_backward_sampled():
+def test_cols_down_backward_full():
+    """dY and X of the down projection's backward, [32768, 7168] with 16
+    groups: every column-wise code, packed scale byte and padded offset."""
     d = W.moe_down_backward(seed=0, device=DEV)
-    off = d["offsets"]
-    off_dev = torch.from_numpy(off).to(DEV)
+    off_dev = torch.from_numpy(d["offsets"]).to(DEV)
     for name in ("dy", "x"):
         x = d[name]
-        M, N = x.shape
         qT, sT, P = mx.mx_quantize_cols(x, off_dev)
         torch.cuda.synchronize()
-        Mcap = qT.shape[1]
-        cols = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(1).integers(0, N, 24)]))
-        sub = bits(x[:, torch.from_numpy(cols).to(DEV)])
-        q_ref, s_ref, P_ref = oracle.quantize_cols(sub, off, Mcap)
-        assert np.array_equal(P.cpu().numpy(), P_ref)
-        assert np.array_equal(u8(qT[torch.from_numpy(cols).to(DEV)]), q_ref)
-        s_all = canonical_scales(sT, N, Mcap)
-        assert np.array_equal(s_all[cols], s_ref)
+        assert_cols_are_oracle(x, d["offsets"], qT, sT, P)
 
 
-def test_cols_quant_bandwidth_sampled():
+def test_cols_quant_bandwidth_full():
     """The quantize-bandwidth workload [131072, 7168] column-wise with no
     groups, as the benchmark runs it: a grid of 512 x 112 workgroups, which
     takes the 256-thread variant of the kernel (smaller grids take the
-    512-thread one).  Sampled transposed rows (= columns of x), all 131072
-    positions each, against the oracle."""
+    512-thread one).  Every code and packed scale byte against the oracle."""
     x = W.quant_bandwidth(seed=0, device=DEV)
     M, N = x.shape
     qT, sT, P = mx.mx_quantize_cols(x)
     torch.cuda.synchronize()
     Mcap = qT.shape[1]
+    assert P is None
     assert Mcap == M and (Mcap // 256) * ((N + 63) // 64) >= 32768
-    cols = np.unique(np.concatenate([[0, 1, 63, 64, N - 1], np.random.default_rng(2).integers(0, N, 24)]))
-    idx = torch.from_numpy(cols).to(DEV)
-    q_ref, s_ref, _ = oracle.quantize_cols(bits(x[:, idx]), None, Mcap)
-    assert np.array_equal(u8(qT[idx]), q_ref)
-    s_all = canonical_scales(sT, N, Mcap)
-    assert np.array_equal(s_all[cols], s_ref)
+    assert_cols_are_oracle(x, None, qT, sT)
 
 
 def test_stream21_calibration_kernel():
