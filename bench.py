@@ -314,6 +314,9 @@ def bench_quant(torch, mx, W, args):
     return res, sample
 
 
+GEMM_CASES = ("gate_up", "swiglu", "ragged", "down")
+
+
 def tflops(M, N, K, ms):
     return 2.0 * M * N * K / (ms * 1e-3) / 1e12
 
@@ -328,6 +331,20 @@ def bench_gemm(torch, mx, W, args):
         torch.cuda.synchronize()
         return tm.run(fn, args.steps)
 
+    cases = set(args.gemm_cases.split(","))
+    unknown = cases - set(GEMM_CASES)
+    if unknown:
+        raise SystemExit(f"bench.py: unknown GEMM case(s) {sorted(unknown)}; choose from {GEMM_CASES}")
+    if cases & {"gate_up", "swiglu"}:
+        gate_up_cases(torch, mx, W, args, timed, cases, out)
+    if "ragged" in cases:
+        ragged_case(torch, mx, W, args, timed, out)
+    if "down" in cases:
+        down_case(torch, mx, W, args, timed, out)
+    return out
+
+
+def gate_up_cases(torch, mx, W, args, timed, cases, out):
     # gate+up projection, 16 experts
     d = W.moe_gate_up(seed=args.seed, device="cuda")
     G, N, K = d["G"], d["N"], d["K"]
@@ -335,14 +352,19 @@ def bench_gemm(torch, mx, W, args):
     Wq, Ws = mx.mx_quantize_rows(d["w"].reshape(G * N, K))
     Wq = Wq.reshape(G, N, K)
     off = torch.from_numpy(d["offsets"]).to("cuda")
-    y = torch.empty((d["M"], N), dtype=torch.bfloat16, device="cuda")
-    ms = timed(lambda: mx.mx_grouped_gemm(Xq, Xs, Wq, Ws, off, out=y))
-    qx = timed(lambda: mx.mx_quantize_rows(d["x"], Xq, Xs))
-    out["gate_up"] = {"M": d["M"], "N": N, "K": K, "G": G, "ms": ms, "tflops": tflops(d["M"], N, K, ms),
-                      "frac_mfma_peak": tflops(d["M"], N, K, ms) / MFMA_FP8_PEAK_TFLOPS,
-                      "quantize_x_ms": qx, "quantize_over_gemm": qx / ms}
-    del Wq, Ws, y
+    ms = None
+    if "gate_up" in cases:
+        y = torch.empty((d["M"], N), dtype=torch.bfloat16, device="cuda")
+        ms = timed(lambda: mx.mx_grouped_gemm(Xq, Xs, Wq, Ws, off, out=y))
+        qx = timed(lambda: mx.mx_quantize_rows(d["x"], Xq, Xs))
+        out["gate_up"] = {"M": d["M"], "N": N, "K": K, "G": G, "ms": ms, "tflops": tflops(d["M"], N, K, ms),
+                          "frac_mfma_peak": tflops(d["M"], N, K, ms) / MFMA_FP8_PEAK_TFLOPS,
+                          "quantize_x_ms": qx, "quantize_over_gemm": qx / ms}
+        del y
+    del Wq, Ws
     torch.cuda.empty_cache()
+    if "swiglu" not in cases:
+        return
 
     # the same projection with the quantizing SwiGLU epilogue: h = silu(gate) up
     # as MXFP8 [M, N/2] + scales instead of bf16 [M, N]
@@ -355,7 +377,7 @@ def bench_gemm(torch, mx, W, args):
     out["gate_up_swiglu"] = {
         "M": d["M"], "N": N, "K": K, "G": G, "ms": ms_sw, "tflops": tflops(d["M"], N, K, ms_sw),
         "frac_mfma_peak": tflops(d["M"], N, K, ms_sw) / MFMA_FP8_PEAK_TFLOPS,
-        "over_bf16_gemm": ms_sw / ms,
+        "over_bf16_gemm": None if ms is None else ms_sw / ms,
         # bytes of the activation written by the fused kernel, and those of
         # the unfused route (bf16 [M, N] written, read back, codes + scales written)
         "bytes_out_fused": d["M"] * I * (1 + 1 / 32),
@@ -364,6 +386,8 @@ def bench_gemm(torch, mx, W, args):
     del d, Xq, Xs, Wi, Wis, hq, hs
     torch.cuda.empty_cache()
 
+
+def ragged_case(torch, mx, W, args, timed, out):
     # ragged 128 experts vs dense
     d = W.moe_ragged(seed=args.seed, device="cuda")
     G, N, K, M = d["G"], d["N"], d["K"], d["M"]
@@ -388,6 +412,8 @@ def bench_gemm(torch, mx, W, args):
     del d, Xq, Xs, Wq, Ws, Dq, Ds, y
     torch.cuda.empty_cache()
 
+
+def down_case(torch, mx, W, args, timed, out):
     # down projection forward / dgrad / wgrad
     d = W.moe_down_backward(seed=args.seed, device="cuda")
     G, N, K, M = d["G"], d["N"], d["K"], d["M"]
@@ -416,7 +442,6 @@ def bench_gemm(torch, mx, W, args):
     }
     del d
     torch.cuda.empty_cache()
-    return out
 
 
 def bench_layer(torch, mx, W, args):
@@ -486,6 +511,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-gemm", action="store_true", help="skip the grouped-GEMM section")
     ap.add_argument("--no-layer", action="store_true", help="skip the MoE-layer chain")
+    ap.add_argument("--gemm-cases", default=",".join(GEMM_CASES),
+                    help="comma-separated subset of the GEMM section's workloads to run (%(default)s); "
+                         "a profiler run of one case sees only its dispatches")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows-1t", type=int, default=8192,
                     help="rows of the one-thread oracle figure (the threaded figure runs the whole input)")
@@ -540,7 +568,7 @@ def main():
             "file": f"profiles/{kname}_trace.txt"},
     }
     roofline_gemm = None
-    if gemm is not None:
+    if gemm is not None and "gate_up" in gemm:
         gu = gemm["gate_up"]
         flops = 2.0 * gu["M"] * gu["N"] * gu["K"]
         gdigest = source_digest(*KERNEL_SOURCES["grouped_gemm"])
@@ -555,6 +583,12 @@ def main():
             "traffic": profile_float(gpmc, "hbm_bytes_per_launch"),
             "algorithmic_flops_per_launch": flops,
             "mfma_busy": profile_float(gpmc, "mfma_busy"),
+            # the shader clock the chip held during this kernel (GRBM_GUI_ACTIVE
+            # cycles per XCD over the dispatch time, from the counter profile):
+            # the 5.0 PFLOP/s peak assumes 2.4 GHz
+            "clock_ghz": profile_float(gpmc, "clock_ghz"),
+            "frac_of_peak_at_clock": None if profile_float(gpmc, "clock_ghz") is None else
+            flops / (gu["ms"] * 1e-3) / 1e12 / (MFMA_FP8_PEAK_TFLOPS * profile_float(gpmc, "clock_ghz") / 2.4),
             "timing": "mean launch time from HIP events on the launch stream over the timed launches of this run",
             "source_sha256": gdigest,
             "kernel_trace": None if gtrace_us is None else {
