@@ -317,6 +317,21 @@ def bench_quant(torch, mx, W, args):
 GEMM_CASES = ("gate_up", "swiglu", "ragged", "down")
 
 
+def tile_stats(torch, sizes, N):
+    """Work decomposition of a row-grouped GEMM launch: every group padded to
+    whole 256-row tiles, 256-column tiles, one persistent workgroup per CU
+    taking one tile per round."""
+    import numpy as np
+
+    sizes = np.asarray(sizes, np.int64)
+    row_tiles = int(((sizes + 255) // 256).sum())
+    tiles = row_tiles * ((N + 255) // 256)
+    wgs = min(torch.cuda.get_device_properties(0).multi_processor_count, tiles) if tiles else 0
+    return {"row_tiles": row_tiles, "padded_rows_frac": row_tiles * 256 / max(int(sizes.sum()), 1) - 1,
+            "tiles": tiles, "workgroups": wgs, "rounds": tiles / wgs if wgs else 0.0,
+            "rounds_run": -(-tiles // wgs) if wgs else 0}
+
+
 def tflops(M, N, K, ms):
     return 2.0 * M * N * K / (ms * 1e-3) / 1e12
 
@@ -359,7 +374,8 @@ def gate_up_cases(torch, mx, W, args, timed, cases, out):
         qx = timed(lambda: mx.mx_quantize_rows(d["x"], Xq, Xs))
         out["gate_up"] = {"M": d["M"], "N": N, "K": K, "G": G, "ms": ms, "tflops": tflops(d["M"], N, K, ms),
                           "frac_mfma_peak": tflops(d["M"], N, K, ms) / MFMA_FP8_PEAK_TFLOPS,
-                          "quantize_x_ms": qx, "quantize_over_gemm": qx / ms}
+                          "quantize_x_ms": qx, "quantize_over_gemm": qx / ms,
+                          "work": tile_stats(torch, d["sizes"], N)}
         del y
     del Wq, Ws
     torch.cuda.empty_cache()
@@ -408,7 +424,8 @@ def ragged_case(torch, mx, W, args, timed, out):
                      "roofline_ms": roof_ms, "frac_roofline_grouped": roof_ms / ms_g,
                      "tflops_grouped": tflops(M, N, K, ms_g), "tflops_dense": tflops(M, N, K, ms_d),
                      "grouped_over_dense": ms_g / ms_d,
-                     "frac_mfma_peak_grouped": tflops(M, N, K, ms_g) / MFMA_FP8_PEAK_TFLOPS}
+                     "frac_mfma_peak_grouped": tflops(M, N, K, ms_g) / MFMA_FP8_PEAK_TFLOPS,
+                     "work_grouped": tile_stats(torch, d["sizes"], N), "work_dense": tile_stats(torch, [M], N)}
     del d, Xq, Xs, Wq, Ws, Dq, Ds, y
     torch.cuda.empty_cache()
 
@@ -435,7 +452,7 @@ def down_case(torch, mx, W, args, timed, out):
     ms_qc = timed(lambda: mx.mx_quantize_cols(d["dy"], off, A.shape[1], A, As, P))
     out["down_backward"] = {
         "M": M, "N": N, "K": K, "G": G,
-        "ms_fwd": ms_f, "tflops_fwd": tflops(M, N, K, ms_f),
+        "ms_fwd": ms_f, "tflops_fwd": tflops(M, N, K, ms_f), "work_fwd": tile_stats(torch, d["sizes"], N),
         "ms_dgrad": ms_dg, "tflops_dgrad": tflops(M, K, N, ms_dg),
         "ms_wgrad": ms_wg, "tflops_wgrad": tflops(N, K, M, ms_wg),
         "quantize_cols_dy_ms": ms_qc,
