@@ -269,6 +269,23 @@ mx_status mx_validate_offsets(const int32_t* group_offsets, int32_t G, int64_t M
  */
 mx_status mx_stream21(const void* src, void* dst, int64_t dst_bytes, void* stream);
 
+/*
+ * Matrix-instruction diagnostic (not a step of the method): T independent
+ * v_mfma_scale_f32_32x32x64_f8f6f4 operations, one per wave, on
+ * caller-given operands, so that tests can pin how the instruction rounds the
+ * block-scaled products and sums that every grouped GEMM entry point is built
+ * from (the scaled product of aigc.bar "拥抱原生硬件指令": block scales applied
+ * by the matrix instruction itself).  For t < T and m, n < 32:
+ *   D[t][m][n] = C[t][m][n] + sum_{k<64} e4m3(A[t][m][k]) e4m3(B[t][n][k])
+ *                             2^(SA[t][m][k/32] - 127) 2^(SB[t][n][k/32] - 127)
+ * as the instruction computes it.  A, B: uint8 E4M3 codes [T][32][64]; SA,
+ * SB: uint8 scale bytes [T][32][2]; C, D: float32 [T][32][32], row-major;
+ * all device memory.  0 <= T <= 65536 (MX_ERR_SHAPE); A, B, C, D 16-byte
+ * aligned (MX_ERR_ALIGN).
+ */
+mx_status mx_probe_mfma_scale(const uint8_t* A, const uint8_t* B, const uint8_t* SA, const uint8_t* SB,
+                              const float* C, float* D, int32_t T, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,6 +57,8 @@ def load():
     lib.mx_validate_offsets.restype = ST
     lib.mx_stream21.argtypes = [P, P, I64, P]
     lib.mx_stream21.restype = ST
+    lib.mx_probe_mfma_scale.argtypes = [P, P, P, P, P, P, I32, P]
+    lib.mx_probe_mfma_scale.restype = ST
     lib.mx_grouped_gemm_dgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, I64, P, P]
     lib.mx_grouped_gemm_dgrad.restype = ST
     lib.mx_grouped_gemm_wgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, P]
@@ -69,7 +71,7 @@ def load():
 SYMBOLS = (
     "mx_status_str", "mx_version", "mx_scale_bytes", "mx_cols_capacity", "mx_quantize_rows",
     "mx_quantize_cols", "mx_quantize_dual", "mx_grouped_gemm", "mx_grouped_gemm_swiglu", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad",
-    "mx_swiglu_backward", "mx_validate_offsets", "mx_stream21",
+    "mx_swiglu_backward", "mx_validate_offsets", "mx_stream21", "mx_probe_mfma_scale",
 )
 
 
@@ -260,6 +262,24 @@ def mx_stream21(src, dst, stream=None):
     rc = load().mx_stream21(_ptr(src), _ptr(dst), dst.numel() * dst.element_size(), _stream(stream))
     _check(rc, "mx_stream21")
     return dst
+
+
+def mx_probe_mfma_scale(A, B, SA, SB, C, out=None, stream=None):
+    """Diagnostic: D[t] = C[t] + the scaled fp8 product of A[t] [32, 64] and
+    B[t] [32, 64] (row n of B = column n of the product), one matrix
+    instruction per t, as the hardware rounds it.  A, B uint8 [T, 32, 64];
+    SA, SB uint8 [T, 32, 2]; C float32 [T, 32, 32]."""
+    T = A.shape[0]
+    if (A.shape != (T, 32, 64) or B.shape != (T, 32, 64) or SA.shape != (T, 32, 2) or SB.shape != (T, 32, 2)
+            or C.shape != (T, 32, 32) or C.dtype != torch.float32):
+        raise ValueError("shapes: A, B [T, 32, 64] uint8; SA, SB [T, 32, 2] uint8; C [T, 32, 32] float32")
+    if not all(t.is_contiguous() for t in (A, B, SA, SB, C)):
+        raise ValueError("contiguous tensors required")
+    if out is None:
+        out = torch.empty_like(C)
+    rc = load().mx_probe_mfma_scale(_ptr(A), _ptr(B), _ptr(SA), _ptr(SB), _ptr(C), _ptr(out), T, _stream(stream))
+    _check(rc, "mx_probe_mfma_scale")
+    return out
 
 
 def mx_grouped_gemm_dgrad(dYq, dYs, WTq, WTs, group_offsets, G, out=None, stream=None):

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmxmoe.so")
-SOURCES = ["api.cpp", "quantize.hip", "quantize_dual.hip", "grouped_gemm.hip", "swiglu_backward.hip", "stream.hip", "offsets.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "quantize_dual.hip", "grouped_gemm.hip", "swiglu_backward.hip", "stream.hip", "offsets.hip", "probe.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -6,6 +6,12 @@
 
 #include "mx_internal.h"
 
+namespace mx {
+// probe.hip (diagnostic of the matrix instruction; not a step of the method)
+hipError_t launch_mfma_probe(const uint8_t* A, const uint8_t* B, const uint8_t* SA, const uint8_t* SB, const float* C,
+                             float* D, int32_t T, hipStream_t stream);
+}  // namespace mx
+
 namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -197,6 +203,15 @@ mx_status mx_stream21(const void* src, void* dst, int64_t dst_bytes, void* strea
     // one lane per 2 granules (16 bytes read, 8 written each): work-items < 2^32
     if (dst_bytes / 16 >= ((int64_t)1 << 32) - 256) return MX_ERR_UNSUPPORTED;
     return from_hip(mx::launch_stream21(src, dst, dst_bytes, (hipStream_t)stream));
+}
+
+mx_status mx_probe_mfma_scale(const uint8_t* A, const uint8_t* B, const uint8_t* SA, const uint8_t* SB,
+                              const float* C, float* D, int32_t T, void* stream) {
+    if (T < 0 || T > 65536) return MX_ERR_SHAPE;
+    if (T == 0) return MX_OK;
+    if (!A || !B || !SA || !SB || !C || !D) return MX_ERR_NULL;
+    if (!aligned16(A) || !aligned16(B) || !aligned16(C) || !aligned16(D)) return MX_ERR_ALIGN;
+    return from_hip(mx::launch_mfma_probe(A, B, SA, SB, C, D, T, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -159,6 +159,16 @@ def test_stream21_validation():
     assert f(FAKE, FAKE, 16 << 32, None) == 5              # 2^32 lanes: over the grid limit
 
 
+def test_probe_mfma_scale_validation():
+    f = mx.load().mx_probe_mfma_scale
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1, None) == 2           # T < 0
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 65537, None) == 2        # over 65536 waves
+    assert f(FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, None) == 1            # NULL B
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, 4, None) == 1            # NULL D
+    assert f(FAKE, FAKE, FAKE, FAKE, P(0x100004), FAKE, 4, None) == 3     # misaligned C
+    assert f(None, None, None, None, None, None, 0, None) == 0            # T == 0
+
+
 def test_dgrad_validation():
     f = mx.load().mx_grouped_gemm_dgrad
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 512, 64, 512, 1024, FAKE, None) == 4   # Wcap < G*K
