@@ -40,7 +40,8 @@
  * Conventions
  *  - Every pointer argument is a DEVICE pointer owned by the caller.  The
  *    library allocates nothing, keeps no state, never synchronizes and never
- *    reads device data on the host.  Every call is asynchronous on `stream`
+ *    reads device data on the host (mx_debug_flags of the debug build
+ *    excepted).  Every call is asynchronous on `stream`
  *    (a hipStream_t; NULL = the default stream).
  *  - Host-checkable preconditions are validated before any launch; a
  *    failing call returns an error code and launches nothing.  A launch
@@ -176,9 +177,11 @@ mx_status mx_grouped_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* W
  *           themselves (bf16 of the fp32 accumulators, columns in the
  *           interleaved order of Wq's rows), as the backward pass of SwiGLU
  *           needs them; 16-byte aligned
- * Rows of a group are written once; rows outside every group, and the
- * scale bytes of the padding rows [M, 32 ceil(M / 32)), are left untouched
- * (no output row reads them).  Requires K % 256 == 0, K > 0 and I % 128 == 0
+ * Rows of a group are written once; rows outside every group, the scale
+ * bytes of the padding rows [M, 32 ceil(M / 32)) and, when I % 256 == 128,
+ * those of the padding blocks [I / 32, 8 ceil(I / 256)) of every row are left
+ * untouched (no output reads them: as a contraction, I must be a multiple of
+ * 256 for the grouped GEMM entry points).  Requires K % 256 == 0, K > 0 and I % 128 == 0
  * (MX_ERR_UNSUPPORTED otherwise), 1 <= G <= 4096, 16-byte aligned pointers.
  */
 mx_status mx_grouped_gemm_swiglu(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq,
@@ -285,6 +288,21 @@ mx_status mx_stream21(const void* src, void* dst, int64_t dst_bytes, void* strea
  */
 mx_status mx_probe_mfma_scale(const uint8_t* A, const uint8_t* B, const uint8_t* SA, const uint8_t* SB,
                               const float* C, float* D, int32_t T, void* stream);
+
+/*
+ * Debug build (libmxmoe_debug.so, compiled with MXMOE_DEBUG): the kernels
+ * that take group offsets check their device-side contract and record
+ * violations; this call synchronizes `stream`, then writes to *flags (a HOST
+ * pointer) the OR of the violations recorded since the last call, and clears
+ * them.  Bits: 1 = group offsets not 0 <= o[0] <= ... <= o[G] <= M (the
+ * rule of mx_validate_offsets); 2 = padded offsets not multiples of 256, not
+ * increasing by each group's padded size, or past the capacity; 4 = a work
+ * tile with no rows of its group.  The checks only record: the kernels clamp
+ * malformed offsets either way.  The release library returns
+ * MX_ERR_UNSUPPORTED with *flags = 0 (no checks compiled in).  Unlike every
+ * other entry point this one synchronizes.  MX_ERR_NULL for flags == NULL.
+ */
+mx_status mx_debug_flags(uint32_t* flags, void* stream);
 
 #ifdef __cplusplus
 }

@@ -13,7 +13,11 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmxmoe.so")
+# MXMOE_DEBUG=1 loads the debug build (device-side contract checks, read with
+# debug_flags()); otherwise the release build
+RELEASE_LIB_PATH = os.path.join(_HERE, "libmxmoe.so")
+DEBUG_LIB_PATH = os.path.join(_HERE, "libmxmoe_debug.so")
+LIB_PATH = DEBUG_LIB_PATH if os.environ.get("MXMOE_DEBUG") == "1" else RELEASE_LIB_PATH
 
 MX_OK = 0
 _lib = None
@@ -28,11 +32,16 @@ class MxError(RuntimeError):
 def load():
     """Load libmxmoe.so (built by ``python -m mxfp8_block_scaled_04_amd.build``)."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"libmxmoe.so not built ({LIB_PATH}); run python -m mxfp8_block_scaled_04_amd.build")
-    lib = ctypes.CDLL(LIB_PATH)
+    if _lib is None:
+        _lib = open_library(LIB_PATH)
+    return _lib
+
+
+def open_library(path):
+    """ctypes handle of a libmxmoe build at `path`, with the C signatures set."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{os.path.basename(path)} not built ({path}); run python -m mxfp8_block_scaled_04_amd.build")
+    lib = ctypes.CDLL(path)
     P, I64, I32, ST = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
     lib.mx_status_str.argtypes = [ctypes.c_int]
     lib.mx_status_str.restype = ctypes.c_char_p
@@ -59,11 +68,12 @@ def load():
     lib.mx_stream21.restype = ST
     lib.mx_probe_mfma_scale.argtypes = [P, P, P, P, P, P, I32, P]
     lib.mx_probe_mfma_scale.restype = ST
+    lib.mx_debug_flags.argtypes = [P, P]
+    lib.mx_debug_flags.restype = ST
     lib.mx_grouped_gemm_dgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, I64, P, P]
     lib.mx_grouped_gemm_dgrad.restype = ST
     lib.mx_grouped_gemm_wgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P, P]
     lib.mx_grouped_gemm_wgrad.restype = ST
-    _lib = lib
     return lib
 
 
@@ -71,7 +81,7 @@ def load():
 SYMBOLS = (
     "mx_status_str", "mx_version", "mx_scale_bytes", "mx_cols_capacity", "mx_quantize_rows",
     "mx_quantize_cols", "mx_quantize_dual", "mx_grouped_gemm", "mx_grouped_gemm_swiglu", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad",
-    "mx_swiglu_backward", "mx_validate_offsets", "mx_stream21", "mx_probe_mfma_scale",
+    "mx_swiglu_backward", "mx_validate_offsets", "mx_stream21", "mx_probe_mfma_scale", "mx_debug_flags",
 )
 
 
@@ -280,6 +290,17 @@ def mx_probe_mfma_scale(A, B, SA, SB, C, out=None, stream=None):
     rc = load().mx_probe_mfma_scale(_ptr(A), _ptr(B), _ptr(SA), _ptr(SB), _ptr(C), _ptr(out), T, _stream(stream))
     _check(rc, "mx_probe_mfma_scale")
     return out
+
+
+def mx_debug_flags(stream=None):
+    """Debug build only: synchronizes the stream and returns (and clears) the
+    contract violations the kernels recorded (bit 1 group offsets, 2 padded
+    offsets, 4 empty work tile); raises MxError(MX_ERR_UNSUPPORTED) on the
+    release build."""
+    flags = ctypes.c_uint32(0)
+    rc = load().mx_debug_flags(ctypes.byref(flags), _stream(stream))
+    _check(rc, "mx_debug_flags")
+    return int(flags.value)
 
 
 def mx_grouped_gemm_dgrad(dYq, dYs, WTq, WTs, group_offsets, G, out=None, stream=None):

@@ -10,6 +10,12 @@ namespace mx {
 // probe.hip (diagnostic of the matrix instruction; not a step of the method)
 hipError_t launch_mfma_probe(const uint8_t* A, const uint8_t* B, const uint8_t* SA, const uint8_t* SB, const float* C,
                              float* D, int32_t T, hipStream_t stream);
+#ifdef MXMOE_DEBUG
+// the debug build's error words, one per code object (mx_debug.h)
+hipError_t debug_take_quantize(uint32_t* out);
+hipError_t debug_take_dual(uint32_t* out);
+hipError_t debug_take_gemm(uint32_t* out);
+#endif
 }  // namespace mx
 
 namespace {
@@ -212,6 +218,25 @@ mx_status mx_probe_mfma_scale(const uint8_t* A, const uint8_t* B, const uint8_t*
     if (!A || !B || !SA || !SB || !C || !D) return MX_ERR_NULL;
     if (!aligned16(A) || !aligned16(B) || !aligned16(C) || !aligned16(D)) return MX_ERR_ALIGN;
     return from_hip(mx::launch_mfma_probe(A, B, SA, SB, C, D, T, (hipStream_t)stream));
+}
+
+mx_status mx_debug_flags(uint32_t* flags, void* stream) {
+    if (!flags) return MX_ERR_NULL;
+    *flags = 0;
+#ifdef MXMOE_DEBUG
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MX_ERR_HIP;
+    uint32_t all = 0;
+    for (hipError_t (*take)(uint32_t*) : {mx::debug_take_quantize, mx::debug_take_dual, mx::debug_take_gemm}) {
+        uint32_t w = 0;
+        if (take(&w) != hipSuccess) return MX_ERR_HIP;
+        all |= w;
+    }
+    *flags = all;
+    return MX_OK;
+#else
+    (void)stream;
+    return MX_ERR_UNSUPPORTED;
+#endif
 }
 
 }  // extern "C"

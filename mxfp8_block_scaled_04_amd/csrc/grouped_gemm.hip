@@ -35,6 +35,7 @@
 //    shares operands through its own L2.
 #include "mx_device.h"
 #include "mx_internal.h"
+#include "mx_debug.h"
 
 namespace mx {
 
@@ -441,6 +442,7 @@ __device__ __forceinline__ Tile decode_tile(const GemmArgs& a, const Layout& L, 
         const int64_t nt = r / gm;
         arow0 = o0 + mt * TM;
         arows = o1 - arow0;
+        debug_flag(arows <= 0, kDbgTile);
         k0 = 0;
         k1 = a.K;
         if (a.mode == 0) {
@@ -711,6 +713,14 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs a) {
         for (int j = 0; j < 16; ++j) {
             const int g = t * 16 + j;
             int32_t cnt = 0;
+            if (g <= G) {
+                if (a.mode != 1) {
+                    debug_flag(offsets_entry_bad(a.offsets, g, G, a.M), kDbgOffsets);
+                } else {
+                    const int64_t p = a.offsets[g];
+                    debug_flag(p % 256 != 0 || p < 0 || p > a.Mcap || (g < G && a.offsets[g + 1] < p), kDbgPadded);
+                }
+            }
             if (g < G) {
                 if (a.mode != 1) {
                     const int64_t lo = group_lo(a.offsets, g, a.M), hi = group_lo(a.offsets, g + 1, a.M);
@@ -894,6 +904,10 @@ void launch(const GemmArgs& a, int64_t nwg, hipStream_t stream) {
 int64_t scale_bytes(int64_t R, int64_t K) { return ((R + 31) / 32) * 32 * (8 * ((K + 255) / 256)); }
 
 }  // namespace
+
+#ifdef MXMOE_DEBUG
+hipError_t debug_take_gemm(uint32_t* out) { return debug_take_word(out); }
+#endif
 
 hipError_t launch_grouped_gemm(const uint8_t* Xq, const uint8_t* Xs, const uint8_t* Wq,
                                const uint8_t* Ws, const int32_t* group_offsets, int32_t G, int64_t M,

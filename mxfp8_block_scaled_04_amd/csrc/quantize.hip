@@ -9,6 +9,7 @@
 // 2 B and write 1 + 1/32 B per element once, with 16-byte coalesced loads.
 #include "mx_device.h"
 #include "mx_internal.h"
+#include "mx_debug.h"
 
 namespace mx {
 
@@ -94,6 +95,7 @@ __global__ __launch_bounds__(1024) void cols_prefix_kernel(const int32_t* __rest
     for (int j = 0; j < 4; ++j) {
         const int g = 4 * t + j;
         int32_t pad = 0;
+        if (g <= G) debug_flag(offsets_entry_bad(off, g, G, M), kDbgOffsets);
         if (g < G) {
             const int32_t a = clamp_off(off, g, M), b = clamp_off(off, g + 1, M);
             const int32_t mg = b > a ? b - a : 0;
@@ -117,7 +119,10 @@ __global__ __launch_bounds__(1024) void cols_prefix_kernel(const int32_t* __rest
         if (g <= G) P[g] = run;
         run += loc[j];
     }
-    if (t == 1023 && G == 4 * 1024) P[G] = run;  // the one entry past every slice
+    if (t == 1023 && G == 4 * 1024) {  // the one entry past every slice
+        P[G] = run;
+        debug_flag(offsets_entry_bad(off, G, G, M), kDbgOffsets);
+    }
 }
 
 // One workgroup handles padded column tile pt (256 rows of one group) x 64
@@ -171,6 +176,12 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(const uint1
             const int64_t o0 = clamp_off(off, g, M), o1 = clamp_off(off, g + 1, M);
             row_begin = o0 + (col0 - P[g]);
             row_end = o1;
+            if (t == 0) {
+                const int64_t mg = o1 > o0 ? o1 - o0 : 0;
+                debug_flag(P[g] % 256 != 0 || P[g + 1] - P[g] != ((mg + 255) / 256) * 256 || P[g + 1] > Mcap,
+                           kDbgPadded);
+                debug_flag(row_begin >= row_end, kDbgTile);
+            }
         }
     }
     // ---- load + transpose into LDS (1024 pair tasks)
@@ -227,6 +238,10 @@ __global__ __launch_bounds__(kColsThreads) void quantize_cols_kernel(const uint1
         }
     }
 }
+
+#ifdef MXMOE_DEBUG
+hipError_t debug_take_quantize(uint32_t* out) { return debug_take_word(out); }
+#endif
 
 hipError_t launch_cols_prefix(const int32_t* group_offsets, int32_t G, int64_t M, int32_t* padded_offsets,
                               hipStream_t stream) {

@@ -8,6 +8,7 @@
 // are pure memory traffic, so reading the input once saves a third of it).
 #include "mx_device.h"
 #include "mx_internal.h"
+#include "mx_debug.h"
 
 namespace mx {
 
@@ -74,6 +75,12 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(const uint16_t* __re
             const int64_t o0 = clamp_off(off, g, M), o1 = clamp_off(off, g + 1, M);
             row_begin = o0 + (col0 - P[g]);
             row_end = o1;
+            if (t == 0) {
+                const int64_t mg = o1 > o0 ? o1 - o0 : 0;
+                debug_flag(P[g] % 256 != 0 || P[g + 1] - P[g] != ((mg + 255) / 256) * 256 || P[g + 1] > Mcap,
+                           kDbgPadded);
+                debug_flag(row_begin >= row_end, kDbgTile);
+            }
         }
     }
     const int c8 = t & 7;  // 16-byte column chunk (8 columns) of a sub-tile
@@ -202,6 +209,10 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(const uint16_t* __re
         dst[32] = 0u;
     }
 }
+
+#ifdef MXMOE_DEBUG
+hipError_t debug_take_dual(uint32_t* out) { return debug_take_word(out); }
+#endif
 
 hipError_t launch_quantize_dual(const uint16_t* x, int64_t M, int64_t N, int64_t ldx,
                                 const int32_t* group_offsets, int32_t G, uint8_t* q, uint8_t* s, uint8_t* qT,

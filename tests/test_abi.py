@@ -33,6 +33,16 @@ def test_library_exports_every_header_symbol():
     assert sorted(mx.SYMBOLS) == names
 
 
+def test_debug_build_exports_and_release_has_no_checks():
+    dbg = mx.open_library(mx.DEBUG_LIB_PATH)
+    for n in header_functions():
+        assert hasattr(dbg, n), n
+    rel = mx.open_library(mx.RELEASE_LIB_PATH)
+    flags = ctypes.c_uint32(7)
+    assert rel.mx_debug_flags(ctypes.byref(flags), None) == 5 and flags.value == 0  # MX_ERR_UNSUPPORTED
+    assert rel.mx_debug_flags(None, None) == 1
+
+
 def test_host_helpers():
     assert mx.mx_scale_bytes(40, 512) == 1024
     assert mx.mx_scale_bytes(131072, 7168) == 131072 * 224
