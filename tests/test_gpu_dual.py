@@ -102,3 +102,23 @@ def test_dual_quant_bandwidth_full():
     assert P is None
     assert_rows_are_oracle(x, q, s)
     assert_cols_are_oracle(x, None, qT, sT)
+
+
+def test_dual_element_map_exhaustive():
+    """The exhaustive (bf16 pattern, scale) blocks through the dual kernel in
+    both orientations: its row-wise result of X and its column-wise result of
+    X^T must both be exactly the oracle's row-wise result of X."""
+    from tests.test_gpu_quantize import _exhaustive_blocks, transposed_padded
+
+    xb = _exhaustive_blocks()
+    R, K = xb.shape
+    q_ref, s_ref = oracle.quantize_rows(xb)
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(DEV)
+    q, s, _, _, _ = prefilled_dual(x, None)
+    assert np.array_equal(u8(q), q_ref), np.argwhere(u8(q) != q_ref)[:5]
+    assert np.array_equal(u8(s), oracle.pack_scales(s_ref, K))
+    xT = transposed_padded(xb, 32)
+    _, _, qT, sT, _ = prefilled_dual(xT, None)
+    assert qT.shape[1] == K
+    assert np.array_equal(u8(qT)[:R], q_ref), np.argwhere(u8(qT)[:R] != q_ref)[:5]
+    assert np.array_equal(canonical_scales(sT, qT.shape[0], K)[:R], s_ref)

@@ -87,6 +87,31 @@ def test_rows_element_map_exhaustive():
     assert set(np.unique(s_ref).tolist()) == set(range(0, 247))
 
 
+def transposed_padded(xb, mult=32):
+    """xb^T as a contiguous bf16 tensor, columns padded with zeros to a
+    multiple of `mult` (the column-wise result's rows are then xb's rows)."""
+    R, K = xb.shape
+    Rp = -(-R // mult) * mult
+    t = np.zeros((K, Rp), np.uint16)
+    t[:, :R] = xb.T
+    return torch.from_numpy(t.view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def test_cols_element_map_exhaustive():
+    """The exhaustive (bf16 pattern, scale) blocks quantized along columns:
+    cols(X^T) must give exactly the oracle's row-wise result of X."""
+    xb = _exhaustive_blocks()
+    R, K = xb.shape
+    xT = transposed_padded(xb, 8)
+    qT, sT, _ = mx.mx_quantize_cols(xT)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_rows(xb)
+    Mcap = qT.shape[1]
+    assert Mcap == K
+    assert np.array_equal(u8(qT)[:R], q_ref), np.argwhere(u8(qT)[:R] != q_ref)[:5]
+    assert np.array_equal(canonical_scales(sT, qT.shape[0], Mcap)[:R], s_ref)
+
+
 def test_rows_quant_bandwidth_full():
     """The quantize-bandwidth workload [131072, 7168] row-wise, as the
     benchmark runs it: every code and every packed scale byte against the
