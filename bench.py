@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the MXFP8 hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--seed S] [--no-gemm] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--seed S] [--no-gemm] [--no-layer] [--no-cpu]
+                    [--gemm-cases gate_up,swiglu,ragged,down] [--copy-calibration]
 
 Prints ONE JSON line.  The headline (``value``) is the quantize bandwidth on
 the quantize-only workload, bf16 [131072, 7168] ~ N(0,1) with 0.1 % of the
@@ -28,8 +29,14 @@ re-quantized each step) and reports each stage's time and the quantize /
 GEMM time ratio.
 
 ``roofline`` describes the dominant kernel of the step (its own launch time
-from HIP events on the launch stream); ``cpu_baseline`` times the CPU oracle
-on a bounded sample of the same workload (a reported baseline, not a target).
+from HIP events on the launch stream, next to the average of the committed
+rocprofv3 kernel trace and the HBM bytes of the committed counter profile,
+both keyed by a hash of the kernel's sources); ``roofline_gemm`` does the
+same for the gate+up GEMM, with the MFMA busy fraction and the shader clock
+the chip held during it.  Each GEMM case also reports its work decomposition
+(256 x 256 tiles, rounds of one tile per CU, row padding).  ``cpu_baseline``
+times the CPU oracle on the whole quantize input (and on one thread over a
+part of it): a reported baseline, not a target.
 """
 import argparse
 import concurrent.futures
