@@ -510,13 +510,27 @@ def bench_layer(torch, mx, W, args):
             stage[names[i]] = stage.get(names[i], 0.0) + events[i - 1].elapsed_time(events[i]) / args.steps
     tm = Timer(torch)
     ms_step = tm.run(step, args.steps)
+    # the same step recorded once as a HIP graph and replayed (every call it
+    # makes only launches kernels on the current stream)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    ms_graph = tm.run(graph.replay, args.steps)
+    del graph
     kinds = {}
     for n, ms in stage.items():
         kinds[KIND[n]] = kinds.get(KIND[n], 0.0) + ms
     quant_act = sum(ms for n, ms in stage.items() if KIND[n] == "quant" and not n.startswith("W"))
     out = {
         "workload": f"MoE layer fwd+bwd, M {M}, H {H}, I {I}, {layer.G} experts (Dirichlet(0.5) routing)",
-        "ms_step": ms_step, "tflops": layer.flops() / (ms_step * 1e-3) / 1e12,
+        "ms_step": ms_step, "tflops": layer.flops() / (ms_step * 1e-3) / 1e12, "ms_step_graph": ms_graph,
         "ms_by_kind": kinds, "ms_by_stage": stage,
         "quant_activations_ms": quant_act,
         "quant_activations_over_gemm": quant_act / kinds["gemm"],

@@ -1,0 +1,68 @@
+"""The MoE-layer step captured as a HIP graph (torch.cuda.CUDAGraph): every
+entry point it calls only launches kernels on the given stream and
+allocates nothing, so the whole forward + backward chain can be recorded
+once and replayed.  Each replay, with eager work and synchronizations
+between replays (the outputs are cleared by eager kernels first, so a
+replay that skipped a write would show), must reproduce the eager step bit
+for bit."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_block_scaled_04_amd as mx
+from mxfp8_block_scaled_04_amd import workloads as W
+from mxfp8_block_scaled_04_amd.moe_layer import MoELayer
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    mx.load()
+
+
+def outputs(layer):
+    """The step's results that every step writes in full."""
+    return {"y": layer.y, "dx": layer.dx, "dW1": layer.dW1, "dW2": layer.dW2, "hq": layer.hq,
+            "preact": layer.preact, "dpre": layer.dpre, "h": layer.h}
+
+
+def bits_of(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+
+def test_layer_step_graph_replays_match_eager():
+    M, H, I, G = 4096, 512, 256, 8
+    sizes = W.dirichlet_sizes(M, G, 0.5, 21)
+    off = torch.from_numpy(W.offsets_from_sizes(sizes)).to(DEV)
+    X = W.normal_bf16((M, H), 1.0, 22, DEV)
+    dY = W.normal_bf16((M, H), 1.0, 23, DEV)
+    W1 = mx.swiglu_interleave(W.normal_bf16((G, 2 * I, H), 1.2 / np.sqrt(H), 24, DEV))
+    W2 = W.normal_bf16((G, H, I), 1.2 / np.sqrt(I), 25, DEV)
+    layer = MoELayer(off, M, H, I)
+
+    layer.step(X, dY, W1, W2)
+    torch.cuda.synchronize()
+    want = {k: v.clone() for k, v in outputs(layer).items()}
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.step(X, dY, W1, W2)  # warm-up on the capture stream's side
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer.step(X, dY, W1, W2)
+    torch.cuda.synchronize()
+
+    for rep in range(3):
+        for t in outputs(layer).values():
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in outputs(layer).items():
+            assert torch.equal(bits_of(v), bits_of(want[k])), f"replay {rep}: {k} differs from the eager step"
