@@ -153,6 +153,32 @@ def test_gemm_group_permutation_bitwise():
     assert np.array_equal(a, b), int(np.count_nonzero(a != b))
 
 
+def test_gemm_ragged_expert_permutation_bitwise_full():
+    """The ragged workload (65536 x 2048 x 7168, 128 Zipf experts with empty
+    and 1-31-row groups) in the benchmark's launch configuration, its experts
+    permuted together with their row blocks: every output element of the
+    permuted run equals the original's permuted row, bit for bit (a check of
+    the expert-aware tile order over the whole output, next to the oracle
+    sample of the ragged parity test)."""
+    d = W.moe_ragged(seed=0, device=DEV)
+    sizes, off = d["sizes"], d["offsets"]
+    G, N, K, M = d["G"], d["N"], d["K"], d["M"]
+    perm = np.random.default_rng(9).permutation(G)
+    off_p = W.offsets_from_sizes([int(sizes[g]) for g in perm])
+    rows_p = torch.from_numpy(np.concatenate([np.arange(off[g], off[g + 1]) for g in perm]).astype(np.int64)).to(DEV)
+    outs = []
+    for xx, ww, oo in ((d["x"], d["w"], off), (d["x"][rows_p], d["w"][torch.from_numpy(perm).to(DEV)], off_p)):
+        Xq, Xs = mx.mx_quantize_rows(xx.contiguous())
+        Wq, Ws = mx.mx_quantize_rows(ww.contiguous().reshape(G * N, K))
+        outs.append(mx.mx_grouped_gemm(Xq, Xs, Wq.reshape(G, N, K), Ws, torch.from_numpy(oo).to(DEV),
+                                       out=nan_filled((M, N))))
+        del Xq, Xs, Wq, Ws
+    torch.cuda.synchronize()
+    a = outs[0][rows_p].view(torch.int16)
+    b = outs[1].view(torch.int16)
+    assert torch.equal(a, b), int((a != b).sum())
+
+
 def test_gemm_zero_rows_is_noop():
     Xq = torch.empty((0, 256), dtype=torch.uint8, device=DEV)
     Xs = torch.empty(0, dtype=torch.uint8, device=DEV)
