@@ -179,6 +179,37 @@ def test_gemm_ragged_expert_permutation_bitwise_full():
     assert torch.equal(a, b), int((a != b).sum())
 
 
+def test_down_backward_expert_permutation_bitwise_full():
+    """dgrad and wgrad of the down projection (32768 rows, 16 Dirichlet
+    experts, 7168 x 2048) in the benchmark's launch configuration, experts
+    permuted together with their row blocks: dX rows and dW experts permute
+    bit for bit over the whole outputs (the wgrad longest-first order changes
+    with the permutation, the results may not)."""
+    d = W.moe_down_backward(seed=0, device=DEV)
+    sizes, off = d["sizes"], d["offsets"]
+    G, N, K, M = d["G"], d["N"], d["K"], d["M"]
+    perm = np.random.default_rng(10).permutation(G)
+    off_p = W.offsets_from_sizes([int(sizes[g]) for g in perm])
+    rows_p = torch.from_numpy(np.concatenate([np.arange(off[g], off[g + 1]) for g in perm]).astype(np.int64)).to(DEV)
+    perm_t = torch.from_numpy(perm).to(DEV)
+    woff = torch.arange(0, G + 1, dtype=torch.int32, device=DEV) * N
+    res = []
+    for dy, x, w, oo in ((d["dy"], d["x"], d["w"], off), (d["dy"][rows_p], d["x"][rows_p], d["w"][perm_t], off_p)):
+        o = torch.from_numpy(oo).to(DEV)
+        dyq, dys = mx.mx_quantize_rows(dy.contiguous())
+        wT, wTs, _ = mx.mx_quantize_cols(w.contiguous().reshape(G * N, K), woff)
+        dx = mx.mx_grouped_gemm_dgrad(dyq, dys, wT, wTs, o, G, out=nan_filled((M, K)))
+        A, As, P = mx.mx_quantize_cols(dy.contiguous(), o)
+        B, Bs, _ = mx.mx_quantize_cols(x.contiguous(), o)
+        dW = mx.mx_grouped_gemm_wgrad(A, As, B, Bs, P, dW=nan_filled((G * N, K)).view(G, N, K))
+        res.append((dx, dW))
+        del dyq, dys, wT, wTs, A, As, B, Bs
+    torch.cuda.synchronize()
+    (dx0, dW0), (dx1, dW1) = res
+    assert torch.equal(dx0[rows_p].view(torch.int16), dx1.view(torch.int16))
+    assert torch.equal(dW0[perm_t].view(torch.int16), dW1.view(torch.int16))
+
+
 def test_gemm_zero_rows_is_noop():
     Xq = torch.empty((0, 256), dtype=torch.uint8, device=DEV)
     Xs = torch.empty(0, dtype=torch.uint8, device=DEV)
