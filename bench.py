@@ -117,7 +117,7 @@ class Timer:
 
 def host_threads():
     """Host threads the oracle may use: the CPUs this process may run on,
-    at most 16 (the GPU machine's CPU share per GPU)."""
+    at most 16 (the host CPU share that goes with one GPU of an 8-GPU node)."""
     try:
         visible = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -560,7 +560,7 @@ def main():
                          "so that HBM counters can be scaled against a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
               "sharding over several GPUs is a design note, not code", file=sys.stderr)
         sys.exit(2)
 

@@ -25,7 +25,7 @@ def host_threads():
         n = len(os.sched_getaffinity(0))
     except AttributeError:
         n = os.cpu_count() or 1
-    # the GPU machine's CPU share is 16 threads per GPU
+    # at most 16: the host CPU share that goes with one GPU of an 8-GPU node
     return max(1, min(n, 16))
 
 
