@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the MXFP8 hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--seed S] [--no-gemm] [--no-layer] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--seed S] [--no-gemm] [--no-layer] [--no-layer-unfused] [--no-cpu]
                     [--gemm-cases gate_up,swiglu,ragged,down] [--copy-calibration]
 
 Prints ONE JSON line.  The headline (``value``) is the quantize bandwidth on
@@ -24,9 +24,10 @@ projection forward / dgrad / wgrad.
 
 ``moe_layer`` runs one MoE layer's expert computation forward + backward on
 that routing (quantize, gate+up GEMM with the quantizing SwiGLU epilogue, down
-GEMM; then dgrad, wgrad, SwiGLU backward and their quantizations; weights
-re-quantized each step) and reports each stage's time and the quantize /
-GEMM time ratio.
+GEMM; then dgrad, the SwiGLU backward fused with the quantization of its
+results, wgrad; weights re-quantized each step) and reports each stage's time
+and the quantize / GEMM time ratio, next to the same step with the SwiGLU
+backward and its quantizations as separate calls.
 
 ``roofline`` describes the dominant kernel of the step (its own launch time
 from HIP events on the launch stream, next to the average of the committed
@@ -472,7 +473,9 @@ def bench_layer(torch, mx, W, args):
     """One MoE layer's expert computation, forward + backward, on the gate+up /
     down workloads' routing (32768 rows, H 7168, I 2048, 16 experts): per-stage
     GPU time from events recorded between the calls, averaged over the timed
-    steps, plus the step total timed without them."""
+    steps, plus the step total timed without them, eagerly and replayed from a
+    HIP graph.  The layer runs with its fused SwiGLU backward + quantization;
+    the same step with that stage unfused is timed after it for comparison."""
     from mxfp8_block_scaled_04_amd.moe_layer import KIND, MoELayer
 
     d1 = W.moe_gate_up(seed=args.seed, device="cuda")
@@ -485,58 +488,71 @@ def bench_layer(torch, mx, W, args):
     off = torch.from_numpy(d1["offsets"]).to("cuda")
     del d1, d2
     torch.cuda.empty_cache()
-    layer = MoELayer(off, M, H, I)
-    step = lambda mark=None: layer.step(X, dY, W1, W2, mark)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    names, events = [], []
-
-    def mark(name):
-        ev = torch.cuda.Event(enable_timing=True)
-        ev.record()
-        names.append(name)
-        events.append(ev)
-
-    stage = {}
-    for _ in range(args.steps):
-        names.clear()
-        events.clear()
-        mark("start")
-        step(mark)
-        events[-1].synchronize()
-        for i in range(1, len(events)):
-            stage[names[i]] = stage.get(names[i], 0.0) + events[i - 1].elapsed_time(events[i]) / args.steps
     tm = Timer(torch)
-    ms_step = tm.run(step, args.steps)
-    # the same step recorded once as a HIP graph and replayed (every call it
-    # makes only launches kernels on the current stream)
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
-    torch.cuda.synchronize()
-    ms_graph = tm.run(graph.replay, args.steps)
-    del graph
+
+    def run(fuse):
+        layer = MoELayer(off, M, H, I, fuse_swiglu_backward=fuse)
+        step = lambda mark=None: layer.step(X, dY, W1, W2, mark)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        names, events = [], []
+
+        def mark(name):
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record()
+            names.append(name)
+            events.append(ev)
+
+        stage = {}
+        for _ in range(args.steps):
+            names.clear()
+            events.clear()
+            mark("start")
+            step(mark)
+            events[-1].synchronize()
+            for i in range(1, len(events)):
+                stage[names[i]] = stage.get(names[i], 0.0) + events[i - 1].elapsed_time(events[i]) / args.steps
+        ms_step = tm.run(step, args.steps)
+        # the same step recorded once as a HIP graph and replayed (every call
+        # it makes only launches kernels on the current stream)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        ms_graph = tm.run(graph.replay, args.steps)
+        flops, G = layer.flops(), layer.G
+        del graph, layer
+        torch.cuda.empty_cache()
+        return stage, ms_step, ms_graph, flops, G
+
+    stage, ms_step, ms_graph, flops, G = run(True)
+    unfused = None
+    if not args.no_layer_unfused:
+        stage_u, ms_step_u, ms_graph_u, _, _ = run(False)
+        unfused = {"ms_step": ms_step_u, "ms_step_graph": ms_graph_u, "ms_by_stage": stage_u}
     kinds = {}
     for n, ms in stage.items():
         kinds[KIND[n]] = kinds.get(KIND[n], 0.0) + ms
+    # quantization of activations and gradients, the fused SwiGLU backward
+    # stage included (its elementwise work is counted with it)
     quant_act = sum(ms for n, ms in stage.items() if KIND[n] == "quant" and not n.startswith("W"))
     out = {
-        "workload": f"MoE layer fwd+bwd, M {M}, H {H}, I {I}, {layer.G} experts (Dirichlet(0.5) routing)",
-        "ms_step": ms_step, "tflops": layer.flops() / (ms_step * 1e-3) / 1e12, "ms_step_graph": ms_graph,
+        "workload": f"MoE layer fwd+bwd, M {M}, H {H}, I {I}, {G} experts (Dirichlet(0.5) routing)",
+        "ms_step": ms_step, "tflops": flops / (ms_step * 1e-3) / 1e12, "ms_step_graph": ms_graph,
         "ms_by_kind": kinds, "ms_by_stage": stage,
         "quant_activations_ms": quant_act,
         "quant_activations_over_gemm": quant_act / kinds["gemm"],
         "quant_all_over_gemm": kinds["quant"] / kinds["gemm"],
+        "unfused_swiglu_backward": unfused,
     }
-    del layer, X, dY, W1, W2
+    del X, dY, W1, W2
     torch.cuda.empty_cache()
     return out
 
@@ -549,6 +565,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-gemm", action="store_true", help="skip the grouped-GEMM section")
     ap.add_argument("--no-layer", action="store_true", help="skip the MoE-layer chain")
+    ap.add_argument("--no-layer-unfused", action="store_true",
+                    help="skip the comparison step of the MoE layer with the SwiGLU backward unfused")
     ap.add_argument("--gemm-cases", default=",".join(GEMM_CASES),
                     help="comma-separated subset of the GEMM section's workloads to run (%(default)s); "
                          "a profiler run of one case sees only its dispatches")

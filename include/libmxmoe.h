@@ -247,6 +247,32 @@ mx_status mx_swiglu_backward(const uint16_t* preact, const uint16_t* dh, int64_t
                              uint16_t* dpre, uint16_t* h, void* stream);
 
 /*
+ * SwiGLU backward fused with the quantizations that the rest of the backward
+ * pass reads (kucoin.com MoK page, section 02, MXFP8 on the data path through
+ * the SwiGLU step; lpnh.cn 2479732 section 1, the backward pass quantizes
+ * along both axes).  Equal, byte for byte, to mx_swiglu_backward(preact, dh)
+ * giving dpre and h, followed by mx_quantize_dual(dpre, group_offsets) and
+ * mx_quantize_cols(h, group_offsets), but neither dpre nor h is written:
+ *   preact, dh   as mx_swiglu_backward (bf16 [M][2I] interleaved gate/up,
+ *                bf16 [M][I])
+ *   q, s         row-wise MXFP8 of d(gate, up): uint8 [M][2I] + packed scales
+ *                (R = M, contraction 2I)
+ *   qT, sT       column-wise MXFP8 of d(gate, up): uint8 [2I][Mcap] + packed
+ *                scales (R = 2I, contraction Mcap)
+ *   hT, hTs      column-wise MXFP8 of h: uint8 [I][Mcap] + packed scales
+ *                (R = I, contraction Mcap)
+ *   padded_offsets  as mx_quantize_cols (one array serves both column-wise
+ *                results)
+ * Group offsets, capacity and padding as mx_quantize_dual.  Requires
+ * I % 128 == 0 (MX_ERR_UNSUPPORTED), Mcap as mx_quantize_cols
+ * (MX_ERR_CAPACITY), 16-byte aligned pointers, 1 <= G <= 4096.
+ */
+mx_status mx_swiglu_backward_quant(const uint16_t* preact, const uint16_t* dh, int64_t M, int64_t I,
+                                   const int32_t* group_offsets, int32_t G, uint8_t* q, uint8_t* s, uint8_t* qT,
+                                   uint8_t* sT, uint8_t* hT, uint8_t* hTs, int64_t Mcap, int32_t* padded_offsets,
+                                   void* stream);
+
+/*
  * Device-side check of a group_offsets array, for callers that want to
  * verify it (the kernels clamp malformed offsets instead of reading out of
  * bounds): valid means 0 <= o[0] <= o[1] <= ... <= o[G] <= M (rows outside

@@ -68,6 +68,8 @@ def open_library(path):
     lib.mx_stream21.restype = ST
     lib.mx_probe_mfma_scale.argtypes = [P, P, P, P, P, P, I32, P]
     lib.mx_probe_mfma_scale.restype = ST
+    lib.mx_swiglu_backward_quant.argtypes = [P, P, I64, I64, P, I32, P, P, P, P, P, P, I64, P, P]
+    lib.mx_swiglu_backward_quant.restype = ST
     lib.mx_debug_flags.argtypes = [P, P]
     lib.mx_debug_flags.restype = ST
     lib.mx_grouped_gemm_dgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, I64, P, P]
@@ -81,7 +83,8 @@ def open_library(path):
 SYMBOLS = (
     "mx_status_str", "mx_version", "mx_scale_bytes", "mx_cols_capacity", "mx_quantize_rows",
     "mx_quantize_cols", "mx_quantize_dual", "mx_grouped_gemm", "mx_grouped_gemm_swiglu", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad",
-    "mx_swiglu_backward", "mx_validate_offsets", "mx_stream21", "mx_probe_mfma_scale", "mx_debug_flags",
+    "mx_swiglu_backward", "mx_swiglu_backward_quant", "mx_validate_offsets", "mx_stream21", "mx_probe_mfma_scale",
+    "mx_debug_flags",
 )
 
 
@@ -250,6 +253,43 @@ def mx_swiglu_backward(preact, dh, dpre=None, h=None, stream=None):
                                    _stream(stream))
     _check(rc, "mx_swiglu_backward")
     return dpre, h
+
+
+def mx_swiglu_backward_quant(preact, dh, group_offsets=None, Mcap=None, q=None, s=None, qT=None, sT=None, hT=None,
+                             hTs=None, padded_offsets=None, stream=None):
+    """SwiGLU backward with its quantizations fused: the results of
+    mx_swiglu_backward (dpre, h) quantized as mx_quantize_dual(dpre) and
+    mx_quantize_cols(h), without dpre or h.  Returns (q, s, qT, sT, hT, hTs,
+    padded_offsets)."""
+    preact, dh = _bits16(preact), _bits16(dh)
+    M, I = dh.shape
+    if preact.shape != (M, 2 * I):
+        raise ValueError("preact must be [M, 2I] for dh [M, I]")
+    if not (preact.is_contiguous() and dh.is_contiguous()):
+        raise ValueError("contiguous tensors required")
+    G = 1 if group_offsets is None else group_offsets.numel() - 1
+    if Mcap is None:
+        Mcap = mx_cols_capacity(M, G)
+    dev = dh.device
+    if q is None:
+        q = torch.empty((M, 2 * I), dtype=torch.uint8, device=dev)
+    if s is None:
+        s = torch.empty(mx_scale_bytes(M, 2 * I), dtype=torch.uint8, device=dev)
+    if qT is None:
+        qT = torch.empty((2 * I, Mcap), dtype=torch.uint8, device=dev)
+    if sT is None:
+        sT = torch.empty(mx_scale_bytes(2 * I, Mcap), dtype=torch.uint8, device=dev)
+    if hT is None:
+        hT = torch.empty((I, Mcap), dtype=torch.uint8, device=dev)
+    if hTs is None:
+        hTs = torch.empty(mx_scale_bytes(I, Mcap), dtype=torch.uint8, device=dev)
+    if group_offsets is not None and padded_offsets is None:
+        padded_offsets = torch.empty(G + 1, dtype=torch.int32, device=dev)
+    rc = load().mx_swiglu_backward_quant(_ptr(preact), _ptr(dh), M, I, _ptr(group_offsets), G, _ptr(q), _ptr(s),
+                                         _ptr(qT), _ptr(sT), _ptr(hT), _ptr(hTs), Mcap, _ptr(padded_offsets),
+                                         _stream(stream))
+    _check(rc, "mx_swiglu_backward_quant")
+    return q, s, qT, sT, hT, hTs, padded_offsets
 
 
 def mx_validate_offsets(group_offsets, M, result=None, stream=None):

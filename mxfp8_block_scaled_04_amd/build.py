@@ -18,7 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmxmoe.so")
 DEBUG_LIB = os.path.join(HERE, "libmxmoe_debug.so")
-SOURCES = ["api.cpp", "quantize.hip", "quantize_dual.hip", "grouped_gemm.hip", "swiglu_backward.hip", "stream.hip", "offsets.hip", "probe.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "quantize_dual.hip", "grouped_gemm.hip", "swiglu_backward.hip", "stream.hip", "offsets.hip", "probe.hip",
+           "swiglu_backward_quant.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

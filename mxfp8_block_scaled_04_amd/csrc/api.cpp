@@ -10,11 +10,17 @@ namespace mx {
 // probe.hip (diagnostic of the matrix instruction; not a step of the method)
 hipError_t launch_mfma_probe(const uint8_t* A, const uint8_t* B, const uint8_t* SA, const uint8_t* SB, const float* C,
                              float* D, int32_t T, hipStream_t stream);
+// swiglu_backward_quant.hip
+hipError_t launch_swiglu_backward_quant(const uint16_t* preact, const uint16_t* dh, int64_t M, int64_t I,
+                                        const int32_t* group_offsets, int32_t G, uint8_t* q, uint8_t* s,
+                                        uint8_t* qT, uint8_t* sT, uint8_t* hT, uint8_t* hTs, int64_t Mcap,
+                                        int32_t* padded_offsets, hipStream_t stream);
 #ifdef MXMOE_DEBUG
 // the debug build's error words, one per code object (mx_debug.h)
 hipError_t debug_take_quantize(uint32_t* out);
 hipError_t debug_take_dual(uint32_t* out);
 hipError_t debug_take_gemm(uint32_t* out);
+hipError_t debug_take_swiglu_quant(uint32_t* out);
 #endif
 }  // namespace mx
 
@@ -195,6 +201,30 @@ mx_status mx_swiglu_backward(const uint16_t* preact, const uint16_t* dh, int64_t
     return from_hip(mx::launch_swiglu_backward(preact, dh, M, I, dpre, h, (hipStream_t)stream));
 }
 
+mx_status mx_swiglu_backward_quant(const uint16_t* preact, const uint16_t* dh, int64_t M, int64_t I,
+                                   const int32_t* group_offsets, int32_t G, uint8_t* q, uint8_t* s, uint8_t* qT,
+                                   uint8_t* sT, uint8_t* hT, uint8_t* hTs, int64_t Mcap, int32_t* padded_offsets,
+                                   void* stream) {
+    if (group_offsets == nullptr) G = 1;
+    if (M < 0 || I < 0 || Mcap < 0) return MX_ERR_SHAPE;
+    if (G < 1 || G > kMaxGroups) return MX_ERR_SHAPE;
+    if (I % 128 != 0) return MX_ERR_UNSUPPORTED;
+    if (Mcap % 256 != 0 || Mcap < mx_cols_capacity(M, G)) return MX_ERR_CAPACITY;
+    if (group_offsets != nullptr && padded_offsets == nullptr) return MX_ERR_NULL;
+    if (I == 0 || Mcap == 0) {
+        if (group_offsets == nullptr) return MX_OK;
+    } else {
+        if (M > 0 && (!preact || !dh || !q || !s)) return MX_ERR_NULL;
+        if (!qT || !sT || !hT || !hTs) return MX_ERR_NULL;
+        if ((preact && !aligned16(preact)) || (dh && !aligned16(dh)) || (q && !aligned16(q)) ||
+            (s && !aligned16(s)) || !aligned16(qT) || !aligned16(sT) || !aligned16(hT) || !aligned16(hTs))
+            return MX_ERR_ALIGN;
+    }
+    if (Mcap / 256 > 65535) return MX_ERR_UNSUPPORTED;  // grid
+    return from_hip(mx::launch_swiglu_backward_quant(preact, dh, M, I, group_offsets, G, q, s, qT, sT, hT, hTs, Mcap,
+                                                     padded_offsets, (hipStream_t)stream));
+}
+
 mx_status mx_validate_offsets(const int32_t* group_offsets, int32_t G, int64_t M, int32_t* result, void* stream) {
     if (G < 1 || G > kMaxGroups || M < 0) return MX_ERR_SHAPE;
     if (!group_offsets || !result) return MX_ERR_NULL;
@@ -226,7 +256,8 @@ mx_status mx_debug_flags(uint32_t* flags, void* stream) {
 #ifdef MXMOE_DEBUG
     if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MX_ERR_HIP;
     uint32_t all = 0;
-    for (hipError_t (*take)(uint32_t*) : {mx::debug_take_quantize, mx::debug_take_dual, mx::debug_take_gemm}) {
+    for (hipError_t (*take)(uint32_t*) :
+         {mx::debug_take_quantize, mx::debug_take_dual, mx::debug_take_gemm, mx::debug_take_swiglu_quant}) {
         uint32_t w = 0;
         if (take(&w) != hipSuccess) return MX_ERR_HIP;
         all |= w;

@@ -12,30 +12,13 @@
 // (4 written without h).
 #include "mx_device.h"
 #include "mx_internal.h"
+#include "mx_swiglu.h"
 
 namespace mx {
 namespace {
 
 __device__ __forceinline__ void store_stream16(void* p, uint4 v) {
     __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
-}
-
-__device__ __forceinline__ float lo_bf16(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float hi_bf16(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
-
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
-}
-
-struct Grad {
-    float dg, du, h;
-};
-
-__device__ __forceinline__ Grad swiglu_grad(float g, float u, float d) {
-    const float sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.44269504088896341f));
-    const float s = g * sig;
-    const float ds = sig * (1.0f + g * (1.0f - sig));
-    return Grad{d * u * ds, d * s, s * u};
 }
 
 // One lane: 8 consecutive hidden units c0 .. c0 + 7 of one row (c0 % 8 == 0):

@@ -19,14 +19,17 @@ of ``swiglu_interleave``; W2 [G, H, I] down weights.
   backward   B1  dY -> row-wise (down dgrad) and column-wise (down wgrad)
                                                       mx_quantize_dual
              B2  dH = dY W2                           mx_grouped_gemm_dgrad
-             B3  d(gate, up) and h from dH and the saved gate/up
-                                                      mx_swiglu_backward
-             B4  h -> column-wise h^T                 mx_quantize_cols
-             B5  dW2 = dY^T h per expert              mx_grouped_gemm_wgrad
-             B6  d(gate, up) -> row-wise and column-wise
-                                                      mx_quantize_dual
-             B7  dX = d(gate, up) W1                  mx_grouped_gemm_dgrad
-             B8  dW1 = d(gate, up)^T X per expert     mx_grouped_gemm_wgrad
+             B3  d(gate, up) and h from dH and the saved gate/up, quantized
+                 as they are made: d(gate, up) row-wise and column-wise, h
+                 column-wise                          mx_swiglu_backward_quant
+             B4  dW2 = dY^T h per expert              mx_grouped_gemm_wgrad
+             B5  dX = d(gate, up) W1                  mx_grouped_gemm_dgrad
+             B6  dW1 = d(gate, up)^T X per expert     mx_grouped_gemm_wgrad
+             With fuse_swiglu_backward=False, B3 is the unfused chain instead:
+             mx_swiglu_backward writes d(gate, up) and h in bf16, then
+             mx_quantize_cols(h) and mx_quantize_dual(d(gate, up)) read them
+             back (the same bytes come out; the fused call saves the bf16
+             round trip through HBM).
   weights    W1, W2 -> row-wise (forward operands) and column-wise (dgrad
              operands, one group per expert)          mx_quantize_dual
 
@@ -36,17 +39,21 @@ buffers once and issues the calls in order on the current stream.
 import torch
 
 from . import (mx_cols_capacity, mx_grouped_gemm, mx_grouped_gemm_dgrad, mx_grouped_gemm_swiglu,
-               mx_grouped_gemm_wgrad, mx_quantize_cols, mx_quantize_dual, mx_scale_bytes, mx_swiglu_backward)
+               mx_grouped_gemm_wgrad, mx_quantize_cols, mx_quantize_dual, mx_scale_bytes, mx_swiglu_backward,
+               mx_swiglu_backward_quant)
 
 FORWARD = ("F1 quantize X", "F2 gate+up GEMM + SwiGLU + quantize", "F3 down GEMM")
-BACKWARD = ("B1 quantize dY", "B2 down dgrad", "B3 SwiGLU backward", "B4 quantize h (cols)", "B5 down wgrad",
-            "B6 quantize d(gate,up)", "B7 gate+up dgrad", "B8 gate+up wgrad")
+BACKWARD = ("B1 quantize dY", "B2 down dgrad", "B3 SwiGLU backward + quantize", "B4 down wgrad",
+            "B5 gate+up dgrad", "B6 gate+up wgrad")
+BACKWARD_UNFUSED = ("B1 quantize dY", "B2 down dgrad", "B3a SwiGLU backward", "B3b quantize h (cols)",
+                    "B3c quantize d(gate,up)", "B4 down wgrad", "B5 gate+up dgrad", "B6 gate+up wgrad")
 WEIGHTS = ("W1 quantize", "W2 quantize")
 KIND = {
     "F1 quantize X": "quant", "F2 gate+up GEMM + SwiGLU + quantize": "gemm", "F3 down GEMM": "gemm",
-    "B1 quantize dY": "quant", "B2 down dgrad": "gemm", "B3 SwiGLU backward": "elementwise",
-    "B4 quantize h (cols)": "quant", "B5 down wgrad": "gemm", "B6 quantize d(gate,up)": "quant",
-    "B7 gate+up dgrad": "gemm", "B8 gate+up wgrad": "gemm", "W1 quantize": "quant", "W2 quantize": "quant",
+    "B1 quantize dY": "quant", "B2 down dgrad": "gemm", "B3 SwiGLU backward + quantize": "quant",
+    "B3a SwiGLU backward": "elementwise", "B3b quantize h (cols)": "quant", "B3c quantize d(gate,up)": "quant",
+    "B4 down wgrad": "gemm", "B5 gate+up dgrad": "gemm", "B6 gate+up wgrad": "gemm",
+    "W1 quantize": "quant", "W2 quantize": "quant",
 }
 
 
@@ -77,8 +84,10 @@ class QuantPair:
 class MoELayer:
     """Buffers and calls of one layer for fixed M, H, I and routing."""
 
-    def __init__(self, offsets, M, H, I, device="cuda"):
+    def __init__(self, offsets, M, H, I, device="cuda", fuse_swiglu_backward=True):
         self.M, self.H, self.I = M, H, I
+        self.fused = fuse_swiglu_backward
+        self.stages = WEIGHTS + FORWARD + (BACKWARD if self.fused else BACKWARD_UNFUSED)
         self.offsets = offsets
         G = self.G = offsets.numel() - 1
         self.woff1 = torch.arange(G + 1, dtype=torch.int32, device=device) * (2 * I)
@@ -92,11 +101,12 @@ class MoELayer:
         self.y = _bf16(M, H, device=device)
         self.dy = QuantPair(M, H, G, device)
         self.dh = _bf16(M, I, device=device)
-        self.dpre = _bf16(M, 2 * I, device=device)
-        self.h = _bf16(M, I, device=device)
+        if not self.fused:  # bf16 d(gate, up) and h exist only in the unfused chain
+            self.dpre = _bf16(M, 2 * I, device=device)
+            self.h = _bf16(M, I, device=device)
+            self.hP = torch.empty(G + 1, dtype=torch.int32, device=device)
         self.hT = _u8(I, self.x.Mcap, device=device)
         self.hTs = _u8(mx_scale_bytes(I, self.x.Mcap), device=device)
-        self.hP = torch.empty(G + 1, dtype=torch.int32, device=device)
         self.dW2 = _bf16(G, H, I, device=device)
         self.dgu = QuantPair(M, 2 * I, G, device)
         self.dx = _bf16(M, H, device=device)
@@ -128,22 +138,29 @@ class MoELayer:
 
     def backward(self, dY, mark=None):
         G = self.G
+        names = BACKWARD if self.fused else BACKWARD_UNFUSED
         self.dy.fill(dY, self.offsets)
-        _mark(mark, BACKWARD[0])
+        _mark(mark, names[0])
         mx_grouped_gemm_dgrad(self.dy.q, self.dy.s, self.w2.qT, self.w2.sT, self.offsets, G, out=self.dh)
-        _mark(mark, BACKWARD[1])
-        mx_swiglu_backward(self.preact, self.dh, dpre=self.dpre, h=self.h)
-        _mark(mark, BACKWARD[2])
-        mx_quantize_cols(self.h, self.offsets, self.x.Mcap, self.hT, self.hTs, self.hP)
-        _mark(mark, BACKWARD[3])
+        _mark(mark, names[1])
+        if self.fused:
+            dgu = self.dgu
+            mx_swiglu_backward_quant(self.preact, self.dh, self.offsets, self.x.Mcap, dgu.q, dgu.s, dgu.qT, dgu.sT,
+                                     self.hT, self.hTs, dgu.P)
+            _mark(mark, names[2])
+        else:
+            mx_swiglu_backward(self.preact, self.dh, dpre=self.dpre, h=self.h)
+            _mark(mark, names[2])
+            mx_quantize_cols(self.h, self.offsets, self.x.Mcap, self.hT, self.hTs, self.hP)
+            _mark(mark, names[3])
+            self.dgu.fill(self.dpre, self.offsets)
+            _mark(mark, names[4])
         mx_grouped_gemm_wgrad(self.dy.qT, self.dy.sT, self.hT, self.hTs, self.dy.P, dW=self.dW2)
-        _mark(mark, BACKWARD[4])
-        self.dgu.fill(self.dpre, self.offsets)
-        _mark(mark, BACKWARD[5])
+        _mark(mark, names[-3])
         mx_grouped_gemm_dgrad(self.dgu.q, self.dgu.s, self.w1.qT, self.w1.sT, self.offsets, G, out=self.dx)
-        _mark(mark, BACKWARD[6])
+        _mark(mark, names[-2])
         mx_grouped_gemm_wgrad(self.dgu.qT, self.dgu.sT, self.x.qT, self.x.sT, self.x.P, dW=self.dW1)
-        _mark(mark, BACKWARD[7])
+        _mark(mark, names[-1])
         return self.dx, self.dW1, self.dW2
 
     def step(self, X, dY, W1, W2, mark=None):

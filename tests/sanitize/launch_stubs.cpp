@@ -46,6 +46,11 @@ hipError_t launch_validate_offsets(const int32_t*, int32_t, int64_t, int32_t*, h
     return hipErrorNotSupported;
 }
 hipError_t launch_stream21(const void*, void*, int64_t, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_swiglu_backward_quant(const uint16_t*, const uint16_t*, int64_t, int64_t, const int32_t*, int32_t,
+                                        uint8_t*, uint8_t*, uint8_t*, uint8_t*, uint8_t*, uint8_t*, int64_t, int32_t*,
+                                        hipStream_t) {
+    return hipErrorNotSupported;
+}
 hipError_t launch_mfma_probe(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, const float*, float*,
                              int32_t, hipStream_t) {
     return hipErrorNotSupported;

@@ -25,15 +25,19 @@ def _gpu():
 
 def outputs(layer):
     """The step's results that every step writes in full."""
-    return {"y": layer.y, "dx": layer.dx, "dW1": layer.dW1, "dW2": layer.dW2, "hq": layer.hq,
-            "preact": layer.preact, "dpre": layer.dpre, "h": layer.h}
+    out = {"y": layer.y, "dx": layer.dx, "dW1": layer.dW1, "dW2": layer.dW2, "hq": layer.hq,
+           "preact": layer.preact, "dh": layer.dh, "dgu.q": layer.dgu.q, "dgu.qT": layer.dgu.qT, "hT": layer.hT}
+    if not layer.fused:
+        out.update(dpre=layer.dpre, h=layer.h)
+    return out
 
 
 def bits_of(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
 
 
-def test_layer_step_graph_replays_match_eager():
+@pytest.mark.parametrize("fuse", [True, False])
+def test_layer_step_graph_replays_match_eager(fuse):
     M, H, I, G = 4096, 512, 256, 8
     sizes = W.dirichlet_sizes(M, G, 0.5, 21)
     off = torch.from_numpy(W.offsets_from_sizes(sizes)).to(DEV)
@@ -41,7 +45,7 @@ def test_layer_step_graph_replays_match_eager():
     dY = W.normal_bf16((M, H), 1.0, 23, DEV)
     W1 = mx.swiglu_interleave(W.normal_bf16((G, 2 * I, H), 1.2 / np.sqrt(H), 24, DEV))
     W2 = W.normal_bf16((G, H, I), 1.2 / np.sqrt(I), 25, DEV)
-    layer = MoELayer(off, M, H, I)
+    layer = MoELayer(off, M, H, I, fuse_swiglu_backward=fuse)
 
     layer.step(X, dY, W1, W2)
     torch.cuda.synchronize()

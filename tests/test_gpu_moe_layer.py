@@ -2,7 +2,11 @@
 each stage's output against the fp64 oracle computed from that stage's own
 GPU inputs, so a wrong buffer or operand anywhere in the chain shows up at
 its stage.  The kernels themselves have their own parity tests; tolerances
-here are theirs (GEMMs: 8e-3 |ref| + 1e-3 rms; quantization: bit-exact)."""
+here are theirs (GEMMs: 8e-3 |ref| + 1e-3 rms; quantization: bit-exact).
+The layer's fused SwiGLU backward + quantization stage is checked against the
+unfused calls (bf16 d(gate, up) and h, then the quantizers) and those against
+the oracle's quantization; the whole step with and without the fusion must
+agree bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -10,7 +14,7 @@ import torch
 import mxfp8_block_scaled_04_amd as mx
 import oracle
 from mxfp8_block_scaled_04_amd import workloads as W
-from mxfp8_block_scaled_04_amd.moe_layer import BACKWARD, FORWARD, WEIGHTS, MoELayer
+from mxfp8_block_scaled_04_amd.moe_layer import BACKWARD, BACKWARD_UNFUSED, FORWARD, WEIGHTS, MoELayer
 from tests.mxtest import bf16_to_f64, bits, canonical_scales, gemm_tolerance_ok, u8
 
 pytestmark = pytest.mark.gpu
@@ -39,21 +43,29 @@ def check_points(got, ref):
     assert ok, ratio
 
 
-def test_moe_layer_chain_stages():
-    sizes = [300, 0, 150, 250]
-    G, H, I = len(sizes), 512, 256
-    M = sum(sizes)
-    off_h = W.offsets_from_sizes(sizes)
+SIZES = [300, 0, 150, 250]
+
+
+def small_layer(fuse):
+    G, H, I = len(SIZES), 512, 256
+    M = sum(SIZES)
+    off_h = W.offsets_from_sizes(SIZES)
     off = torch.from_numpy(off_h).to(DEV)
     X = W.normal_bf16((M, H), 1.0, 1, DEV)
     W1 = mx.swiglu_interleave(W.normal_bf16((G, 2 * I, H), 1.2 / np.sqrt(H), 2, DEV))
     W2 = W.normal_bf16((G, H, I), 0.05, 3, DEV)
     dY = W.normal_bf16((M, H), 1.0, 4, DEV)
-    layer = MoELayer(off, M, H, I)
+    layer = MoELayer(off, M, H, I, fuse_swiglu_backward=fuse)
     seen = []
     layer.step(X, dY, W1, W2, mark=seen.append)
     torch.cuda.synchronize()
-    assert seen == list(WEIGHTS + FORWARD + BACKWARD)
+    assert seen == list(layer.stages)
+    return layer, (X, dY, W1, W2, off, off_h, G, H, I, M)
+
+
+def test_moe_layer_chain_stages():
+    layer, (X, dY, W1, W2, off, off_h, G, H, I, M) = small_layer(True)
+    assert layer.stages == WEIGHTS + FORWARD + BACKWARD
     rng = np.random.default_rng(0)
 
     # weights and F1: bit-exact quantizations
@@ -91,15 +103,22 @@ def test_moe_layer_chain_stages():
     ref = oracle.grouped_gemm_points(q, s, Bq, Bs, off_h, rows, cols)
     check_points(bf16_to_f64(layer.dh)[rows, cols], ref)
 
-    # B3: SwiGLU backward on the saved gate/up and dH
+    # B3: the fused SwiGLU backward + quantization against the unfused calls
+    # on the saved gate/up and dH (bf16 d(gate, up) and h, then quantized)
     dpre, h = mx.mx_swiglu_backward(layer.preact, layer.dh, h=True)
+    dq, ds, dqT, dsT, P = mx.mx_quantize_dual(dpre, off, layer.x.Mcap)
+    hT, hTs, hP = mx.mx_quantize_cols(h, off, layer.x.Mcap)
     torch.cuda.synchronize()
-    assert torch.equal(dpre.view(torch.int16), layer.dpre.view(torch.int16))
-    assert torch.equal(h.view(torch.int16), layer.h.view(torch.int16))
+    assert torch.equal(dq, layer.dgu.q) and torch.equal(dqT, layer.dgu.qT) and torch.equal(hT, layer.hT)
+    assert torch.equal(P, layer.dgu.P) and torch.equal(hP, layer.dgu.P)
+    assert np.array_equal(canonical_scales(ds, M, 2 * I), canonical_scales(layer.dgu.s, M, 2 * I))
+    Mcap = layer.x.Mcap
+    assert np.array_equal(canonical_scales(dsT, 2 * I, Mcap), canonical_scales(layer.dgu.sT, 2 * I, Mcap))
+    assert np.array_equal(canonical_scales(hTs, I, Mcap), canonical_scales(layer.hTs, I, Mcap))
 
-    # B4 + B5: dW2 = dY^T h per expert
-    qT, sT, P = oracle.quantize_cols(bits(layer.h), off_h, layer.x.Mcap)
-    assert np.array_equal(u8(layer.hT), qT)
+    # B3 (h part) + B4: dW2 = dY^T h per expert
+    qT, sT, P = oracle.quantize_cols(bits(h), off_h, layer.x.Mcap)
+    assert np.array_equal(u8(layer.hT), qT) and np.array_equal(layer.dgu.P.cpu().numpy(), P)
     Aq, As = u8(layer.dy.qT), canonical_scales(layer.dy.sT, H, layer.x.Mcap)
     gs = rng.integers(0, G, 1500)
     ns = rng.integers(0, H, 1500)
@@ -107,18 +126,43 @@ def test_moe_layer_chain_stages():
     ref = oracle.wgrad_points(Aq, As, qT, sT, P, gs, ns, ks)
     check_points(bf16_to_f64(layer.dW2)[gs, ns, ks], ref)
 
-    # B6 + B7: dX = d(gate, up) W1
-    q, s = oracle.quantize_rows(bits(layer.dpre))
+    # B3 (d(gate, up) row-wise) + B5: dX = d(gate, up) W1
+    q, s = oracle.quantize_rows(bits(dpre))
     assert np.array_equal(u8(layer.dgu.q), q)
+    assert np.array_equal(canonical_scales(layer.dgu.s, M, 2 * I), s)
     Bq, Bs = wT_operands(layer.w1.qT, layer.w1.sT, G, 2 * I, H)
     cols = rng.integers(0, H, 1500)
     ref = oracle.grouped_gemm_points(q, s, Bq, Bs, off_h, rows, cols)
     check_points(bf16_to_f64(layer.dx)[rows, cols], ref)
 
-    # B8: dW1 = d(gate, up)^T X per expert
-    qT, sT, P = oracle.quantize_cols(bits(layer.dpre), off_h, layer.x.Mcap)
+    # B3 (d(gate, up) column-wise) + B6: dW1 = d(gate, up)^T X per expert
+    qT, sT, P = oracle.quantize_cols(bits(dpre), off_h, layer.x.Mcap)
     assert np.array_equal(u8(layer.dgu.qT), qT)
     ns = rng.integers(0, 2 * I, 1500)
     ks = rng.integers(0, H, 1500)
     ref = oracle.wgrad_points(qT, sT, u8(layer.x.qT), canonical_scales(layer.x.sT, H, layer.x.Mcap), P, gs, ns, ks)
     check_points(bf16_to_f64(layer.dW1)[gs, ns, ks], ref)
+
+
+def test_moe_layer_fused_and_unfused_steps_agree():
+    """The same step with the SwiGLU backward fused and unfused: every
+    quantized buffer and every result bit for bit, and the unfused chain's
+    bf16 intermediates as mx_swiglu_backward makes them."""
+    fused, _ = small_layer(True)
+    plain, (X, dY, W1, W2, off, off_h, G, H, I, M) = small_layer(False)
+    assert plain.stages == WEIGHTS + FORWARD + BACKWARD_UNFUSED
+    for name in ("y", "dh", "dx", "dW1", "dW2", "preact"):
+        a, b = getattr(fused, name), getattr(plain, name)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), name
+    for name in ("hq", "hT"):
+        assert torch.equal(getattr(fused, name), getattr(plain, name)), name
+    assert torch.equal(fused.dgu.q, plain.dgu.q) and torch.equal(fused.dgu.qT, plain.dgu.qT)
+    assert torch.equal(fused.dgu.P, plain.dgu.P)
+    Mcap = plain.x.Mcap
+    assert np.array_equal(canonical_scales(fused.dgu.s, M, 2 * I), canonical_scales(plain.dgu.s, M, 2 * I))
+    assert np.array_equal(canonical_scales(fused.dgu.sT, 2 * I, Mcap), canonical_scales(plain.dgu.sT, 2 * I, Mcap))
+    assert np.array_equal(canonical_scales(fused.hTs, I, Mcap), canonical_scales(plain.hTs, I, Mcap))
+    dpre, h = mx.mx_swiglu_backward(plain.preact, plain.dh, h=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dpre.view(torch.int16), plain.dpre.view(torch.int16))
+    assert torch.equal(h.view(torch.int16), plain.h.view(torch.int16))

@@ -174,6 +174,13 @@ def full_check(x, w, sizes):
         probe = np.zeros((Mpad, nb), np.uint8)
         probe[M:] = 1
         assert np.all(hs_h[oracle.pack_scales(probe, I) == 1] == FILL)
+    # with I % 256 == 128 the packed rows carry 4 padding blocks, left untouched
+    KB = 8 * (-(-I // 256))
+    if KB * 32 > I:
+        r = np.arange(Mpad)[:, None]
+        b = np.arange(I // 32, KB)[None, :]
+        offs = (r // 32) * 32 * KB + (b // 8) * 256 + 4 * (32 * (b % 2) + r % 32) + (b % 8) // 2
+        assert np.all(hs_h[offs] == FILL)
 
 
 @pytest.mark.parametrize("sizes,I,K", [

@@ -101,3 +101,49 @@ def test_swiglu_backward_gate_up_shape_sampled():
     dh = W.normal_bf16((M, I), 1.0, 12, DEV)
     rows = np.sort(np.random.default_rng(13).choice(M, 256, replace=False))
     check(pre, dh, rows=rows)
+
+
+FILL = 0xEE
+
+
+def fused_against_chain(preact, dh, sizes):
+    """mx_swiglu_backward_quant against mx_swiglu_backward followed by
+    mx_quantize_dual of d(gate, up) and mx_quantize_cols of h (each of those
+    checked against the oracle by its own tests), every output prefilled with
+    FILL: every byte, written or left alone, must be the same."""
+    M, I = dh.shape
+    off = None if sizes is None else torch.from_numpy(W.offsets_from_sizes(sizes)).to(DEV)
+    G = 1 if sizes is None else len(sizes)
+    Mcap = mx.mx_cols_capacity(M, G)
+    fill = lambda *shape: torch.full(shape, FILL, dtype=torch.uint8, device=DEV)
+    bufs = lambda: (fill(M, 2 * I), fill(mx.mx_scale_bytes(M, 2 * I)), fill(2 * I, Mcap),
+                    fill(mx.mx_scale_bytes(2 * I, Mcap)), fill(I, Mcap), fill(mx.mx_scale_bytes(I, Mcap)))
+    q, s, qT, sT, hT, hTs = bufs()
+    dpre, h = mx.mx_swiglu_backward(preact, dh, h=True)
+    _, _, _, _, P = mx.mx_quantize_dual(dpre, off, Mcap, q, s, qT, sT)
+    mx.mx_quantize_cols(h, off, Mcap, hT, hTs)
+    f = bufs()
+    got = mx.mx_swiglu_backward_quant(preact, dh, off, Mcap, *f)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("q", "s", "qT", "sT", "hT", "hTs"), (q, s, qT, sT, hT, hTs), got[:6]):
+        assert torch.equal(a, b), f"{name}: {int((a != b).sum())} bytes differ"
+    if P is not None:
+        assert torch.equal(P, got[6])
+
+
+@pytest.mark.parametrize("sizes,I", [([100, 0, 37, 300, 163], 128), ([1, 31, 33, 0, 257, 5], 256), ([513], 384),
+                                     ([0, 0, 64], 128), (None, 128)])
+def test_swiglu_backward_quant_matches_the_chain(sizes, I):
+    M = 300 if sizes is None else sum(sizes)
+    preact = (W.normal_bf16((M, 2 * I), 1.0, 60 + M, DEV).float() * 3).to(torch.bfloat16)
+    dh = W.normal_bf16((M, I), 1.0, 61 + M, DEV)
+    fused_against_chain(preact, dh, sizes)
+
+
+def test_swiglu_backward_quant_layer_shape():
+    """The MoE layer's shape (32768 rows, I = 2048, the 16 Dirichlet groups)."""
+    d = W.moe_gate_up(seed=0, device=DEV)
+    M, I = d["M"], d["N"] // 2
+    preact = (W.normal_bf16((M, 2 * I), 1.0, 70, DEV).float() * 3).to(torch.bfloat16)
+    dh = W.normal_bf16((M, I), 1.0, 71, DEV)
+    fused_against_chain(preact, dh, list(d["sizes"]))
