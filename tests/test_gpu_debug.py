@@ -1,7 +1,8 @@
 """The debug build (libmxmoe_debug.so: the same kernels with MXMOE_DEBUG,
 whose device-side contract checks are read by mx_debug_flags): silent on
 valid inputs, with every output bit-identical to the release build's, and
-recording malformed group offsets and padded offsets.  Malformed offsets are
+recording malformed group offsets and padded offsets (the SwiGLU backward
+with its quantizations fused included).  Malformed offsets are
 safe to run: the kernels clamp them (wrong results, no access out of
 bounds), and the debug checks only record."""
 import numpy as np
@@ -61,6 +62,15 @@ def pipeline(d, off):
     # hs: the scale bytes the contract defines (I = 128: the padding blocks
     # 4-7 of each row are left untouched)
     out["swiglu"] = (hq, pre, torch.from_numpy(oracle.unpack_scales(hs.cpu().numpy(), x.shape[0], N)))
+    # its backward, plain and with the quantizations fused (scales compared
+    # in their canonical form)
+    M = x.shape[0]
+    dh = W.normal_bf16((M, N), 1.0, 7, DEV)
+    out["swiglu_bwd"] = mx.mx_swiglu_backward(pre, dh, h=True)
+    q, s, qT, sT, hT, hTs, P2 = mx.mx_swiglu_backward_quant(pre, dh, off)
+    Mcap = qT.shape[1]
+    canon = lambda t, R, C: torch.from_numpy(oracle.unpack_scales(t.cpu().numpy(), R, C))
+    out["swiglu_bwd_quant"] = (q, qT, hT, P2, canon(s, M, 2 * N), canon(sT, 2 * N, Mcap), canon(hTs, N, Mcap))
     # backward of a projection with 256 outputs (dgrad contracts over them)
     N2 = 256
     w2 = W.normal_bf16((G, N2, K), 0.05, 6, DEV)
@@ -111,6 +121,12 @@ def test_malformed_offsets_recorded(libs):
     assert under(dbg, mx.mx_debug_flags) & 1
     valid = torch.tensor([0, 160, 512], dtype=torch.int32, device=DEV)
     under(dbg, lambda: mx.mx_quantize_cols(x, valid))
+    assert under(dbg, mx.mx_debug_flags) == 0
+    pre = W.normal_bf16((512, 256), 1.0, 8, DEV)
+    dh = W.normal_bf16((512, 128), 1.0, 9, DEV)
+    under(dbg, lambda: mx.mx_swiglu_backward_quant(pre, dh, bad))
+    assert under(dbg, mx.mx_debug_flags) & 1
+    under(dbg, lambda: mx.mx_swiglu_backward_quant(pre, dh, valid))
     assert under(dbg, mx.mx_debug_flags) == 0
 
 
