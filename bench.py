@@ -475,7 +475,9 @@ def bench_layer(torch, mx, W, args):
     GPU time from events recorded between the calls, averaged over the timed
     steps, plus the step total timed without them, eagerly and replayed from a
     HIP graph.  The layer runs with its fused SwiGLU backward + quantization;
-    the same step with that stage unfused is timed after it for comparison."""
+    the step with its independent calls on two streams (``two_streams``) and
+    the step with the SwiGLU backward unfused are timed after it for
+    comparison."""
     from mxfp8_block_scaled_04_amd.moe_layer import KIND, MoELayer
 
     d1 = W.moe_gate_up(seed=args.seed, device="cuda")
@@ -527,15 +529,35 @@ def bench_layer(torch, mx, W, args):
             step()
         torch.cuda.synchronize()
         ms_graph = tm.run(graph.replay, args.steps)
+        del graph
+        overlapped = None
+        if fuse:
+            # the same step with its independent calls on two streams
+            ovl = lambda: layer.step_overlapped(X, dY, W1, W2)
+            for _ in range(args.warmup):
+                ovl()
+            torch.cuda.synchronize()
+            ms_ovl = tm.run(ovl, args.steps)
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                ovl()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                ovl()
+            torch.cuda.synchronize()
+            overlapped = {"ms_step": ms_ovl, "ms_step_graph": tm.run(graph.replay, args.steps)}
+            del graph
         flops, G = layer.flops(), layer.G
-        del graph, layer
+        del layer
         torch.cuda.empty_cache()
-        return stage, ms_step, ms_graph, flops, G
+        return stage, ms_step, ms_graph, flops, G, overlapped
 
-    stage, ms_step, ms_graph, flops, G = run(True)
+    stage, ms_step, ms_graph, flops, G, overlapped = run(True)
     unfused = None
     if not args.no_layer_unfused:
-        stage_u, ms_step_u, ms_graph_u, _, _ = run(False)
+        stage_u, ms_step_u, ms_graph_u, _, _, _ = run(False)
         unfused = {"ms_step": ms_step_u, "ms_step_graph": ms_graph_u, "ms_by_stage": stage_u}
     kinds = {}
     for n, ms in stage.items():
@@ -550,6 +572,7 @@ def bench_layer(torch, mx, W, args):
         "quant_activations_ms": quant_act,
         "quant_activations_over_gemm": quant_act / kinds["gemm"],
         "quant_all_over_gemm": kinds["quant"] / kinds["gemm"],
+        "two_streams": overlapped,
         "unfused_swiglu_backward": unfused,
     }
     del X, dY, W1, W2

@@ -34,7 +34,8 @@ of ``swiglu_interleave``; W2 [G, H, I] down weights.
              operands, one group per expert)          mx_quantize_dual
 
 Every step runs in the library's kernels; this module only allocates the
-buffers once and issues the calls in order on the current stream.
+buffers once and issues the calls in order on the current stream
+(step_overlapped: the independent ones on two streams).
 """
 import torch
 
@@ -167,6 +168,53 @@ class MoELayer:
         self.quantize_weights(W1, W2, mark)
         self.forward(X, mark)
         return self.backward(dY, mark)
+
+    def step_overlapped(self, X, dY, W1, W2):
+        """The same step with its independent calls on two streams (the
+        current one and a second one of default priority), so that a call
+        can start on the workgroup slots another call's last round leaves
+        idle.  Same calls, same buffers, same results bit for bit:
+          current  W1 quantize, quantize X, F2 | F3 (after W2) | B3 (after
+                   B2) | B5, B6
+          second   W2 quantize, B1, B2 | B4 (after B3)
+        The second stream starts after all earlier work on the current one
+        and the current one waits for all of the second's before returning,
+        so consecutive steps never overlap on a buffer."""
+        if not self.fused:
+            raise ValueError("the overlapped step runs the fused SwiGLU backward")
+        G, H, I = self.G, self.H, self.I
+        main = torch.cuda.current_stream()
+        if getattr(self, "_side", None) is None or self._side.device != main.device:
+            self._side = torch.cuda.Stream(device=main.device)
+        side = self._side
+        w2_done = torch.cuda.Event()
+        b2_done = torch.cuda.Event()
+        b3_done = torch.cuda.Event()
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            self.w2.fill(W2.reshape(G * H, I), self.woff2)
+            w2_done.record(side)
+            self.dy.fill(dY, self.offsets)
+            mx_grouped_gemm_dgrad(self.dy.q, self.dy.s, self.w2.qT, self.w2.sT, self.offsets, G, out=self.dh)
+            b2_done.record(side)
+        self.w1.fill(W1.reshape(G * 2 * I, H), self.woff1)
+        self.x.fill(X, self.offsets)
+        mx_grouped_gemm_swiglu(self.x.q, self.x.s, self.w1.q.view(G, 2 * I, H), self.w1.s, self.offsets,
+                               hq=self.hq, hs=self.hs, preact=self.preact)
+        main.wait_event(w2_done)
+        mx_grouped_gemm(self.hq, self.hs, self.w2.q.view(G, H, I), self.w2.s, self.offsets, out=self.y)
+        main.wait_event(b2_done)
+        dgu = self.dgu
+        mx_swiglu_backward_quant(self.preact, self.dh, self.offsets, self.x.Mcap, dgu.q, dgu.s, dgu.qT, dgu.sT,
+                                 self.hT, self.hTs, dgu.P)
+        b3_done.record(main)
+        with torch.cuda.stream(side):
+            side.wait_event(b3_done)
+            mx_grouped_gemm_wgrad(self.dy.qT, self.dy.sT, self.hT, self.hTs, self.dy.P, dW=self.dW2)
+        mx_grouped_gemm_dgrad(dgu.q, dgu.s, self.w1.qT, self.w1.sT, self.offsets, G, out=self.dx)
+        mx_grouped_gemm_wgrad(dgu.qT, dgu.sT, self.x.qT, self.x.sT, self.x.P, dW=self.dW1)
+        main.wait_stream(side)
+        return self.dx, self.dW1, self.dW2
 
 
 def _mark(mark, name):

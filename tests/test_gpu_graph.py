@@ -1,7 +1,8 @@
 """The MoE-layer step captured as a HIP graph (torch.cuda.CUDAGraph): every
 entry point it calls only launches kernels on the given stream and
 allocates nothing, so the whole forward + backward chain can be recorded
-once and replayed.  Each replay, with eager work and synchronizations
+once and replayed (the two-stream step too: its fork and join become graph
+dependencies).  Each replay, with eager work and synchronizations
 between replays (the outputs are cleared by eager kernels first, so a
 replay that skipped a write would show), must reproduce the eager step bit
 for bit."""
@@ -36,8 +37,8 @@ def bits_of(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
 
 
-@pytest.mark.parametrize("fuse", [True, False])
-def test_layer_step_graph_replays_match_eager(fuse):
+@pytest.mark.parametrize("fuse,overlap", [(True, False), (False, False), (True, True)])
+def test_layer_step_graph_replays_match_eager(fuse, overlap):
     M, H, I, G = 4096, 512, 256, 8
     sizes = W.dirichlet_sizes(M, G, 0.5, 21)
     off = torch.from_numpy(W.offsets_from_sizes(sizes)).to(DEV)
@@ -46,20 +47,21 @@ def test_layer_step_graph_replays_match_eager(fuse):
     W1 = mx.swiglu_interleave(W.normal_bf16((G, 2 * I, H), 1.2 / np.sqrt(H), 24, DEV))
     W2 = W.normal_bf16((G, H, I), 1.2 / np.sqrt(I), 25, DEV)
     layer = MoELayer(off, M, H, I, fuse_swiglu_backward=fuse)
+    run = layer.step_overlapped if overlap else layer.step
 
-    layer.step(X, dY, W1, W2)
+    run(X, dY, W1, W2)
     torch.cuda.synchronize()
     want = {k: v.clone() for k, v in outputs(layer).items()}
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        layer.step(X, dY, W1, W2)  # warm-up on the capture stream's side
+        run(X, dY, W1, W2)  # warm-up on the capture stream's side
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        layer.step(X, dY, W1, W2)
+        run(X, dY, W1, W2)
     torch.cuda.synchronize()
 
     for rep in range(3):

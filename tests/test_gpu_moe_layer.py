@@ -166,3 +166,23 @@ def test_moe_layer_fused_and_unfused_steps_agree():
     torch.cuda.synchronize()
     assert torch.equal(dpre.view(torch.int16), plain.dpre.view(torch.int16))
     assert torch.equal(h.view(torch.int16), plain.h.view(torch.int16))
+
+
+def test_moe_layer_overlapped_step_matches_the_sequential_one():
+    """The two-stream step: the same results bit for bit as the one-stream
+    step, on two consecutive steps with the outputs cleared in between (a
+    missing wait between the streams, or between steps, would read a buffer
+    before it is written)."""
+    seq, (X, dY, W1, W2, off, off_h, G, H, I, M) = small_layer(True)
+    ovl = MoELayer(off, M, H, I)
+    for rep in range(2):
+        for t in (ovl.y, ovl.dx, ovl.dW1, ovl.dW2, ovl.dh, ovl.hT, ovl.dgu.q, ovl.dgu.qT):
+            t.zero_()
+        ovl.step_overlapped(X, dY, W1, W2)
+        torch.cuda.synchronize()
+        for name in ("y", "dh", "dx", "dW1", "dW2", "preact"):
+            a, b = getattr(seq, name), getattr(ovl, name)
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), (rep, name)
+        for name in ("hq", "hT"):
+            assert torch.equal(getattr(seq, name), getattr(ovl, name)), (rep, name)
+        assert torch.equal(seq.dgu.q, ovl.dgu.q) and torch.equal(seq.dgu.qT, ovl.dgu.qT), rep
