@@ -62,7 +62,7 @@ def quant_bytes(M, K):
 # sources each kernel is built from (its .hip file and the headers it includes)
 KERNEL_SOURCES = {
     "quantize": ("quantize.hip", "mx_device.h", "mx_internal.h", "mx_debug.h"),
-    "quantize_dual": ("quantize_dual.hip", "mx_device.h", "mx_internal.h", "mx_debug.h"),
+    "quantize_dual": ("quantize_dual.hip", "mx_bf16.h", "mx_device.h", "mx_internal.h", "mx_debug.h"),
     "grouped_gemm": ("grouped_gemm.hip", "mx_device.h", "mx_internal.h", "mx_debug.h"),
 }
 

@@ -273,6 +273,68 @@ mx_status mx_swiglu_backward_quant(const uint16_t* preact, const uint16_t* dh, i
                                    void* stream);
 
 /*
+ * The one-GPU share of expert-parallel dispatch and combine (kucoin.com MoK
+ * page, section 02: the expert side pulls each routed token by its source
+ * position and lays the rows out in local expert order; each expert output
+ * goes back to its token; MXFP8 is applied on the dispatch path).  A routed
+ * entry j = t k + c is choice c of token t; experts[j] is its expert.
+ *
+ * mx_route_plan: a stable counting sort of the entries by expert.
+ *   experts      int32 [T][k], device; entries outside [0, G) are dropped
+ *   weights      NULL, or float [T][k] routing weights (device)
+ *   offsets      int32 [G+1] out: exclusive prefix of the per-expert counts
+ *                (offsets[G] = number of routed entries), the group offsets
+ *                of the expert-ordered rows
+ *   src          int32 [T k] out: src[i] = token of the entry placed in slot
+ *                i, for i < offsets[G] (slots grouped by expert, in entry
+ *                order inside an expert); later entries untouched
+ *   slot_of      int32 [T k] out: the slot of entry j, or -1 when dropped
+ *   slot_weight  NULL, or float [T k] out: weights[j] at slot_of[j] (needs
+ *                weights; MX_ERR_NULL otherwise)
+ * Requires T >= 0, k >= 1, 1 <= G <= 4096 (MX_ERR_SHAPE), T k < 2^31
+ * (MX_ERR_UNSUPPORTED), 4-byte aligned pointers.  Two launches; the second
+ * reads the expert list once per expert (O(G T k) reads, from L2).
+ */
+mx_status mx_route_plan(const int32_t* experts, const float* weights, int64_t T, int32_t k, int32_t G,
+                        int32_t* offsets, int32_t* src, int32_t* slot_of, float* slot_weight, void* stream);
+
+/*
+ * mx_gather_quantize: mx_quantize_dual of the gathered matrix R [M][N] whose
+ * row r is row src[r] of x (T rows, row stride ldx): the dispatch pull with
+ * its quantization (x = token rows, src from mx_route_plan); with a row
+ * scale, R[r][c] = bf16(fp32(row_scale[r] * x[src[r]][c])) (the product in
+ * binary32, then rounded to bf16, each to nearest even), the backward of a
+ * weighted combine (x = output gradient of the tokens, row_scale =
+ * slot_weight).  Rows whose src lies outside [0, T) quantize as zeros.
+ *   src        int32 [M], device (may be NULL when M == 0)
+ *   row_scale  NULL, or float [M], device
+ * Everything else, outputs included, as mx_quantize_dual with M rows
+ * (group_offsets over [0, M], Mcap >= mx_cols_capacity(M, G)); x may be NULL
+ * when T == 0.  Byte for byte equal to mx_quantize_dual of R.
+ */
+mx_status mx_gather_quantize(const uint16_t* x, int64_t T, int64_t N, int64_t ldx, const int32_t* src,
+                             const float* row_scale, int64_t M, const int32_t* group_offsets, int32_t G, uint8_t* q,
+                             uint8_t* s, uint8_t* qT, uint8_t* sT, int64_t Mcap, int32_t* padded_offsets,
+                             void* stream);
+
+/*
+ * mx_combine: out[t][c] = bf16( sum_{i<k} w[t][i] y[slot_of[t][i]][c] ),
+ * the routing-weighted sum of a token's expert outputs (weights == NULL: the
+ * plain sum, the backward of the gather).  The sum runs in fp32 in choice
+ * order (fused multiply-add, one rounding per step) and is rounded to bf16
+ * (nearest even) once; entries whose slot lies outside [0, M) are skipped
+ * (a token with none gets zeros).
+ *   y        bf16 [M][ldy] expert-ordered rows (device; may be NULL when M == 0)
+ *   slot_of  int32 [T][k] (mx_route_plan), weights NULL or float [T][k]
+ *   out      bf16 [T][N], written in full
+ * Requires N % 8 == 0 (MX_ERR_UNSUPPORTED), ldy >= N, k >= 1 (MX_ERR_SHAPE),
+ * y, out 16-byte aligned, ldy % 8 == 0, slot_of and weights 4-byte aligned
+ * (MX_ERR_ALIGN); T < 2^31, N / 2048 < 65536 (MX_ERR_UNSUPPORTED).
+ */
+mx_status mx_combine(const uint16_t* y, int64_t M, int64_t N, int64_t ldy, const int32_t* slot_of,
+                     const float* weights, int64_t T, int32_t k, uint16_t* out, void* stream);
+
+/*
  * Device-side check of a group_offsets array, for callers that want to
  * verify it (the kernels clamp malformed offsets instead of reading out of
  * bounds): valid means 0 <= o[0] <= o[1] <= ... <= o[G] <= M (rows outside

@@ -70,6 +70,12 @@ def open_library(path):
     lib.mx_probe_mfma_scale.restype = ST
     lib.mx_swiglu_backward_quant.argtypes = [P, P, I64, I64, P, I32, P, P, P, P, P, P, I64, P, P]
     lib.mx_swiglu_backward_quant.restype = ST
+    lib.mx_route_plan.argtypes = [P, P, I64, I32, I32, P, P, P, P, P]
+    lib.mx_route_plan.restype = ST
+    lib.mx_gather_quantize.argtypes = [P, I64, I64, I64, P, P, I64, P, I32, P, P, P, P, I64, P, P]
+    lib.mx_gather_quantize.restype = ST
+    lib.mx_combine.argtypes = [P, I64, I64, I64, P, P, I64, I32, P, P]
+    lib.mx_combine.restype = ST
     lib.mx_debug_flags.argtypes = [P, P]
     lib.mx_debug_flags.restype = ST
     lib.mx_grouped_gemm_dgrad.argtypes = [P, P, P, P, P, I32, I64, I64, I64, I64, P, P]
@@ -83,8 +89,8 @@ def open_library(path):
 SYMBOLS = (
     "mx_status_str", "mx_version", "mx_scale_bytes", "mx_cols_capacity", "mx_quantize_rows",
     "mx_quantize_cols", "mx_quantize_dual", "mx_grouped_gemm", "mx_grouped_gemm_swiglu", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad",
-    "mx_swiglu_backward", "mx_swiglu_backward_quant", "mx_validate_offsets", "mx_stream21", "mx_probe_mfma_scale",
-    "mx_debug_flags",
+    "mx_swiglu_backward", "mx_swiglu_backward_quant", "mx_route_plan", "mx_gather_quantize", "mx_combine",
+    "mx_validate_offsets", "mx_stream21", "mx_probe_mfma_scale", "mx_debug_flags",
 )
 
 
@@ -290,6 +296,87 @@ def mx_swiglu_backward_quant(preact, dh, group_offsets=None, Mcap=None, q=None, 
                                          _stream(stream))
     _check(rc, "mx_swiglu_backward_quant")
     return q, s, qT, sT, hT, hTs, padded_offsets
+
+
+def mx_route_plan(experts, G, weights=None, offsets=None, src=None, slot_of=None, slot_weight=None, stream=None):
+    """experts int32 [T, k] (device), G experts (, float32 weights [T, k]) ->
+    (offsets int32 [G+1], src int32 [T k], slot_of int32 [T, k],
+    slot_weight float32 [T k] or None): the stable sort of the routed entries
+    by expert (entries outside [0, G) dropped, slot -1)."""
+    if experts.dtype != torch.int32 or experts.dim() != 2 or not experts.is_contiguous():
+        raise ValueError("experts must be a contiguous int32 [T, k] tensor")
+    T, k = experts.shape
+    dev = experts.device
+    if weights is not None and (weights.dtype != torch.float32 or tuple(weights.shape) != (T, k)
+                                or not weights.is_contiguous()):
+        raise ValueError("weights must be a contiguous float32 [T, k] tensor")
+    if offsets is None:
+        offsets = torch.empty(G + 1, dtype=torch.int32, device=dev)
+    if src is None:
+        src = torch.empty(T * k, dtype=torch.int32, device=dev)
+    if slot_of is None:
+        slot_of = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if weights is not None and slot_weight is None:
+        slot_weight = torch.empty(T * k, dtype=torch.float32, device=dev)
+    rc = load().mx_route_plan(_ptr(experts), _ptr(weights), T, k, G, _ptr(offsets), _ptr(src), _ptr(slot_of),
+                              _ptr(slot_weight), _stream(stream))
+    _check(rc, "mx_route_plan")
+    return offsets, src, slot_of, slot_weight
+
+
+def mx_gather_quantize(x, src, M, group_offsets=None, Mcap=None, row_scale=None, q=None, s=None, qT=None, sT=None,
+                       padded_offsets=None, stream=None):
+    """mx_quantize_dual of the matrix whose row r is x[src[r]] (x bf16 [T, N],
+    src int32 [>= M]), each row optionally scaled by row_scale[r] (float32)
+    in fp32 and rounded to bf16 first.  Returns (q, s, qT, sT, padded_offsets)."""
+    x = _bits16(x)
+    T, N = x.shape
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous")
+    G = 1 if group_offsets is None else group_offsets.numel() - 1
+    if Mcap is None:
+        Mcap = mx_cols_capacity(M, G)
+    if src.dtype != torch.int32 or src.numel() < M:
+        raise ValueError("src must be an int32 tensor of at least M entries")
+    if row_scale is not None and (row_scale.dtype != torch.float32 or row_scale.numel() < M):
+        raise ValueError("row_scale must be a float32 tensor of at least M entries")
+    dev = x.device
+    if q is None:
+        q = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    if s is None:
+        s = torch.empty(mx_scale_bytes(M, N), dtype=torch.uint8, device=dev)
+    if qT is None:
+        qT = torch.empty((N, Mcap), dtype=torch.uint8, device=dev)
+    if sT is None:
+        sT = torch.empty(mx_scale_bytes(N, Mcap), dtype=torch.uint8, device=dev)
+    if group_offsets is not None and padded_offsets is None:
+        padded_offsets = torch.empty(G + 1, dtype=torch.int32, device=dev)
+    rc = load().mx_gather_quantize(_ptr(x), T, N, x.stride(0), _ptr(src), _ptr(row_scale), M, _ptr(group_offsets), G,
+                                   _ptr(q), _ptr(s), _ptr(qT), _ptr(sT), Mcap, _ptr(padded_offsets), _stream(stream))
+    _check(rc, "mx_gather_quantize")
+    return q, s, qT, sT, padded_offsets
+
+
+def mx_combine(y, slot_of, weights=None, out=None, stream=None):
+    """y bf16 [M, N] expert-ordered rows, slot_of int32 [T, k] (, float32
+    weights [T, k]) -> bf16 [T, N]: the weighted (or plain) sum of each
+    token's expert rows."""
+    y = _bits16(y)
+    M, N = y.shape
+    if y.stride(1) != 1:
+        raise ValueError("y rows must be contiguous")
+    if slot_of.dtype != torch.int32 or slot_of.dim() != 2 or not slot_of.is_contiguous():
+        raise ValueError("slot_of must be a contiguous int32 [T, k] tensor")
+    T, k = slot_of.shape
+    if weights is not None and (weights.dtype != torch.float32 or tuple(weights.shape) != (T, k)
+                                or not weights.is_contiguous()):
+        raise ValueError("weights must be a contiguous float32 [T, k] tensor")
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=y.device)
+    rc = load().mx_combine(_ptr(y), M, N, y.stride(0), _ptr(slot_of), _ptr(weights), T, k, _ptr(_bits16(out)),
+                           _stream(stream))
+    _check(rc, "mx_combine")
+    return out
 
 
 def mx_validate_offsets(group_offsets, M, result=None, stream=None):

@@ -19,7 +19,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmxmoe.so")
 DEBUG_LIB = os.path.join(HERE, "libmxmoe_debug.so")
 SOURCES = ["api.cpp", "quantize.hip", "quantize_dual.hip", "grouped_gemm.hip", "swiglu_backward.hip", "stream.hip", "offsets.hip", "probe.hip",
-           "swiglu_backward_quant.hip"]
+           "swiglu_backward_quant.hip", "routing.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -15,6 +15,16 @@ hipError_t launch_swiglu_backward_quant(const uint16_t* preact, const uint16_t* 
                                         const int32_t* group_offsets, int32_t G, uint8_t* q, uint8_t* s,
                                         uint8_t* qT, uint8_t* sT, uint8_t* hT, uint8_t* hTs, int64_t Mcap,
                                         int32_t* padded_offsets, hipStream_t stream);
+// routing.hip and the gathering dual quantizer (quantize_dual.hip)
+hipError_t launch_route_plan(const int32_t* experts, const float* weights, int64_t T, int32_t k, int32_t G,
+                             int32_t* offsets, int32_t* src, int32_t* slot_of, float* slot_weight,
+                             hipStream_t stream);
+hipError_t launch_gather_quantize(const uint16_t* x, int64_t T, int64_t N, int64_t ldx, const int32_t* src,
+                                  const float* row_scale, int64_t M, const int32_t* group_offsets, int32_t G,
+                                  uint8_t* q, uint8_t* s, uint8_t* qT, uint8_t* sT, int64_t Mcap,
+                                  int32_t* padded_offsets, hipStream_t stream);
+hipError_t launch_combine(const uint16_t* y, int64_t M, int64_t N, int64_t ldy, const int32_t* slot_of,
+                          const float* w, int64_t T, int32_t k, uint16_t* out, hipStream_t stream);
 #ifdef MXMOE_DEBUG
 // the debug build's error words, one per code object (mx_debug.h)
 hipError_t debug_take_quantize(uint32_t* out);
@@ -27,6 +37,7 @@ hipError_t debug_take_swiglu_quant(uint32_t* out);
 namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
 
@@ -223,6 +234,57 @@ mx_status mx_swiglu_backward_quant(const uint16_t* preact, const uint16_t* dh, i
     if (Mcap / 256 > 65535) return MX_ERR_UNSUPPORTED;  // grid
     return from_hip(mx::launch_swiglu_backward_quant(preact, dh, M, I, group_offsets, G, q, s, qT, sT, hT, hTs, Mcap,
                                                      padded_offsets, (hipStream_t)stream));
+}
+
+mx_status mx_route_plan(const int32_t* experts, const float* weights, int64_t T, int32_t k, int32_t G,
+                        int32_t* offsets, int32_t* src, int32_t* slot_of, float* slot_weight, void* stream) {
+    if (T < 0 || k < 1) return MX_ERR_SHAPE;
+    if (G < 1 || G > kMaxGroups) return MX_ERR_SHAPE;
+    if (T * (int64_t)k >= ((int64_t)1 << 31)) return MX_ERR_UNSUPPORTED;  // int32 slots
+    if (!offsets) return MX_ERR_NULL;
+    if (T > 0 && (!experts || !src || !slot_of)) return MX_ERR_NULL;
+    if (slot_weight && !weights && T > 0) return MX_ERR_NULL;
+    if (!aligned4(offsets) || (experts && !aligned4(experts)) || (src && !aligned4(src)) ||
+        (slot_of && !aligned4(slot_of)) || (weights && !aligned4(weights)) || (slot_weight && !aligned4(slot_weight)))
+        return MX_ERR_ALIGN;
+    return from_hip(mx::launch_route_plan(experts, weights, T, k, G, offsets, src, slot_of, slot_weight,
+                                          (hipStream_t)stream));
+}
+
+mx_status mx_gather_quantize(const uint16_t* x, int64_t T, int64_t N, int64_t ldx, const int32_t* src,
+                             const float* row_scale, int64_t M, const int32_t* group_offsets, int32_t G, uint8_t* q,
+                             uint8_t* s, uint8_t* qT, uint8_t* sT, int64_t Mcap, int32_t* padded_offsets,
+                             void* stream) {
+    if (group_offsets == nullptr) G = 1;
+    if (T < 0 || M < 0 || N < 0 || N % 32 != 0 || ldx < N || Mcap < 0) return MX_ERR_SHAPE;
+    if (G < 1 || G > kMaxGroups) return MX_ERR_SHAPE;
+    if (Mcap % 256 != 0 || Mcap < mx_cols_capacity(M, G)) return MX_ERR_CAPACITY;
+    if (group_offsets != nullptr && padded_offsets == nullptr) return MX_ERR_NULL;
+    if (N == 0 || Mcap == 0) {
+        if (group_offsets == nullptr) return MX_OK;
+    } else {
+        if ((!x && T > 0) || (!src && M > 0)) return MX_ERR_NULL;
+        if (!qT || !sT || (M > 0 && (!q || !s))) return MX_ERR_NULL;
+        if ((x && !aligned16(x)) || !aligned16(qT) || !aligned16(sT) || (q && !aligned16(q)) ||
+            (s && !aligned16(s)) || ldx % 8 != 0 || (src && !aligned4(src)) || (row_scale && !aligned4(row_scale)))
+            return MX_ERR_ALIGN;
+    }
+    if (Mcap / 256 > 65535 || (N + 255) / 256 > (int64_t)UINT32_MAX / 256) return MX_ERR_UNSUPPORTED;  // grid
+    return from_hip(mx::launch_gather_quantize(x, T, N, ldx, src, row_scale, M, group_offsets,
+                                               G, q, s, qT, sT, Mcap, padded_offsets, (hipStream_t)stream));
+}
+
+mx_status mx_combine(const uint16_t* y, int64_t M, int64_t N, int64_t ldy, const int32_t* slot_of,
+                     const float* weights, int64_t T, int32_t k, uint16_t* out, void* stream) {
+    if (M < 0 || N < 0 || ldy < N || T < 0 || k < 1) return MX_ERR_SHAPE;
+    if (N % 8 != 0) return MX_ERR_UNSUPPORTED;
+    if (T == 0 || N == 0) return MX_OK;
+    if (!slot_of || !out || (M > 0 && !y)) return MX_ERR_NULL;
+    if ((y && !aligned16(y)) || !aligned16(out) || ldy % 8 != 0 || !aligned4(slot_of) ||
+        (weights && !aligned4(weights)))
+        return MX_ERR_ALIGN;
+    if (T > (int64_t)INT32_MAX || (N / 8 + 255) / 256 > 65535) return MX_ERR_UNSUPPORTED;  // grid
+    return from_hip(mx::launch_combine(y, M, N, ldy, slot_of, weights, T, k, out, (hipStream_t)stream));
 }
 
 mx_status mx_validate_offsets(const int32_t* group_offsets, int32_t G, int64_t M, int32_t* result, void* stream) {

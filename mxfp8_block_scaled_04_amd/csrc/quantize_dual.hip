@@ -6,6 +6,7 @@
 // Method (lpnh.cn 2479732 section 1: the backward pass quantizes the same
 // gradient along both axes; aigc.bar "被忽视的量化税": the quantization passes
 // are pure memory traffic, so reading the input once saves a third of it).
+#include "mx_bf16.h"
 #include "mx_device.h"
 #include "mx_internal.h"
 #include "mx_debug.h"
@@ -36,13 +37,21 @@ namespace mx {
 // Every row of a group lies in exactly one row tile; rows in
 // [M, 32 ceil(M / 32)) get zero row-wise scale bytes, and blocks past N read
 // as zeros, so both packed arrays equal those of the separate kernels.
+//
+// GATHER: row r of the quantized matrix is row src[r] of x (T rows), the
+// pull side of an expert-parallel dispatch (kucoin.com MoK page, section
+// 02: MXFP8 applied on the dispatch path); with a row scale, each element is
+// first multiplied by rscale[r] in fp32 and rounded to bf16 (nearest even).
+// Rows whose source index lies outside [0, T) quantize as zeros.
 // ---------------------------------------------------------------------------
+template <bool GATHER>
 __global__ __launch_bounds__(256) void quantize_dual_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t N,
                                                             int64_t ldx, const int32_t* __restrict__ off,
                                                             const int32_t* __restrict__ P, int32_t G,
                                                             uint8_t* __restrict__ q, uint8_t* __restrict__ s,
                                                             uint8_t* __restrict__ qT, uint8_t* __restrict__ sT,
-                                                            int64_t Mcap) {
+                                                            int64_t Mcap, const int32_t* __restrict__ src,
+                                                            const float* __restrict__ rscale, int64_t T) {
     __shared__ uint4 tile[64 * 32];
     __shared__ uint32_t unit_s[2][64];
     __shared__ uint32_t row_s[256][2];  // per tile row: packed dwords of K halves 0 and 1 of the chunk
@@ -85,6 +94,26 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(const uint16_t* __re
     }
     const int c8 = t & 7;  // 16-byte column chunk (8 columns) of a sub-tile
     uint4 da[4], db[4];
+    // GATHER: source rows of this lane's row pairs (-1: none) and their scales
+    int64_t sra[4], srb[4];
+    float fa[4], fb[4];
+    if constexpr (GATHER) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int pr = i * 32 + (t >> 3);
+            const int64_t r0 = row_begin + 2 * pr, r1 = r0 + 1;
+            sra[i] = (g >= 0 && r0 < row_end) ? (int64_t)src[r0] : -1;
+            srb[i] = (g >= 0 && r1 < row_end) ? (int64_t)src[r1] : -1;
+            if (sra[i] >= T) sra[i] = -1;
+            if (srb[i] >= T) srb[i] = -1;
+            fa[i] = (rscale != nullptr && sra[i] >= 0) ? rscale[r0] : 1.0f;
+            fb[i] = (rscale != nullptr && srb[i] >= 0) ? rscale[r1] : 1.0f;
+        }
+    }
+    auto scaled = [&](uint4 v, float f) {
+        return make_uint4(pack_bf16(lo_bf16(v.x) * f, hi_bf16(v.x) * f), pack_bf16(lo_bf16(v.y) * f, hi_bf16(v.y) * f),
+                          pack_bf16(lo_bf16(v.z) * f, hi_bf16(v.z) * f), pack_bf16(lo_bf16(v.w) * f, hi_bf16(v.w) * f));
+    };
     auto load = [&](int st) {
         const int64_t ncol = (ct * 4 + st) * 64 + c8 * 8;
 #pragma unroll
@@ -94,8 +123,22 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(const uint16_t* __re
             da[i] = make_uint4(0, 0, 0, 0);
             db[i] = make_uint4(0, 0, 0, 0);
             if (g >= 0 && ncol < N) {
-                if (r0 < row_end) da[i] = load_stream16(x + r0 * ldx + ncol);
-                if (r1 < row_end) db[i] = load_stream16(x + r1 * ldx + ncol);
+                if constexpr (GATHER) {
+                    if (sra[i] >= 0) da[i] = load_stream16(x + sra[i] * ldx + ncol);
+                    if (srb[i] >= 0) db[i] = load_stream16(x + srb[i] * ldx + ncol);
+                } else {
+                    if (r0 < row_end) da[i] = load_stream16(x + r0 * ldx + ncol);
+                    if (r1 < row_end) db[i] = load_stream16(x + r1 * ldx + ncol);
+                }
+            }
+        }
+        if constexpr (GATHER) {
+            if (rscale != nullptr) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    da[i] = scaled(da[i], fa[i]);
+                    db[i] = scaled(db[i], fb[i]);
+                }
             }
         }
     };
@@ -214,9 +257,10 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(const uint16_t* __re
 hipError_t debug_take_dual(uint32_t* out) { return debug_take_word(out); }
 #endif
 
-hipError_t launch_quantize_dual(const uint16_t* x, int64_t M, int64_t N, int64_t ldx,
-                                const int32_t* group_offsets, int32_t G, uint8_t* q, uint8_t* s, uint8_t* qT,
-                                uint8_t* sT, int64_t Mcap, int32_t* padded_offsets, hipStream_t stream) {
+static hipError_t launch_dual(const uint16_t* x, int64_t M, int64_t N, int64_t ldx, const int32_t* group_offsets,
+                              int32_t G, uint8_t* q, uint8_t* s, uint8_t* qT, uint8_t* sT, int64_t Mcap,
+                              int32_t* padded_offsets, const int32_t* src, const float* rscale, int64_t T,
+                              hipStream_t stream) {
     if (group_offsets != nullptr) {
         hipError_t e = launch_cols_prefix(group_offsets, G, M, padded_offsets, stream);
         if (e != hipSuccess) return e;
@@ -225,9 +269,28 @@ hipError_t launch_quantize_dual(const uint16_t* x, int64_t M, int64_t N, int64_t
     }
     if (N == 0 || Mcap == 0) return hipSuccess;
     dim3 grid((unsigned)((N + 255) / 256), (unsigned)(Mcap / 256));
-    hipLaunchKernelGGL(quantize_dual_kernel, grid, dim3(256), 0, stream, x, M, N, ldx, group_offsets,
-                       (const int32_t*)padded_offsets, G, q, s, qT, sT, Mcap);
+    if (src != nullptr)
+        hipLaunchKernelGGL(quantize_dual_kernel<true>, grid, dim3(256), 0, stream, x, M, N, ldx, group_offsets,
+                           (const int32_t*)padded_offsets, G, q, s, qT, sT, Mcap, src, rscale, T);
+    else
+        hipLaunchKernelGGL(quantize_dual_kernel<false>, grid, dim3(256), 0, stream, x, M, N, ldx, group_offsets,
+                           (const int32_t*)padded_offsets, G, q, s, qT, sT, Mcap, nullptr, nullptr, M);
     return hipGetLastError();
+}
+
+hipError_t launch_quantize_dual(const uint16_t* x, int64_t M, int64_t N, int64_t ldx,
+                                const int32_t* group_offsets, int32_t G, uint8_t* q, uint8_t* s, uint8_t* qT,
+                                uint8_t* sT, int64_t Mcap, int32_t* padded_offsets, hipStream_t stream) {
+    return launch_dual(x, M, N, ldx, group_offsets, G, q, s, qT, sT, Mcap, padded_offsets, nullptr, nullptr, M,
+                       stream);
+}
+
+hipError_t launch_gather_quantize(const uint16_t* x, int64_t T, int64_t N, int64_t ldx, const int32_t* src,
+                                  const float* row_scale, int64_t M, const int32_t* group_offsets, int32_t G,
+                                  uint8_t* q, uint8_t* s, uint8_t* qT, uint8_t* sT, int64_t Mcap,
+                                  int32_t* padded_offsets, hipStream_t stream) {
+    return launch_dual(x, M, N, ldx, group_offsets, G, q, s, qT, sT, Mcap, padded_offsets, src, row_scale, T,
+                       stream);
 }
 
 }  // namespace mx

@@ -67,6 +67,20 @@ def zipf_sizes(total, experts, s, seed, n_empty=8, n_tiny=8):
     return sizes
 
 
+def topk_routing(tokens, k, experts, alpha, seed):
+    """Top-k routing of `tokens` tokens to k distinct experts each: expert
+    popularity p ~ Dirichlet(alpha * 1), each token's experts drawn from p
+    without replacement; routing weights U(0, 1) normalized to sum to 1 per
+    token.  Returns (experts int32 [tokens, k], weights float32 [tokens, k])."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    p = rng.dirichlet(np.full(experts, alpha))
+    e = np.stack([rng.choice(experts, k, replace=False, p=p) for _ in range(tokens)]) if tokens else \
+        np.zeros((0, k), np.int64)
+    w = rng.uniform(0.0, 1.0, (tokens, k))
+    w /= np.maximum(w.sum(axis=1, keepdims=True), 1e-30)
+    return e.astype(np.int32), w.astype(np.float32)
+
+
 # ---------------------------------------------------------------- workloads
 
 

@@ -36,6 +36,12 @@ Parity status of each function (what pins it in ``tests/test_oracle.py``):
                                      float32 values, hand-worked ties, values
                                      past float32 precision (no double rounding)
   swiglu_backward                    zero and saturated gates in closed form
+  route_plan                         brute force (a sort of (expert, entry)
+                                     pairs), histogram offsets, inverse maps
+  f32_round / gather_rows            identity gathers, exact power-of-two
+                                     scales, hand-worked double-rounding cases
+  combine                            one-hot weights reduce to the gather,
+                                     hand-worked sums, linearity in the weights
 """
 import ctypes
 import os
@@ -108,6 +114,11 @@ def _load():
     lib.mxref_bf16_round.restype = ctypes.c_uint16
     lib.mxref_bf16_round_n.argtypes = [P, I64, P]
     lib.mxref_swiglu_backward.argtypes = [P, P, P, I64, P, P, P]
+    lib.mxref_route_plan.argtypes = [P, I64, ctypes.c_int32, ctypes.c_int32, P, P, P]
+    lib.mxref_f32_round.argtypes = [ctypes.c_double]
+    lib.mxref_f32_round.restype = ctypes.c_double
+    lib.mxref_gather_rows.argtypes = [P, I64, I64, P, P, I64, P]
+    lib.mxref_combine.argtypes = [P, I64, I64, P, P, I64, ctypes.c_int32, P]
     _lib = lib
     return lib
 
@@ -351,3 +362,52 @@ def swiglu_backward(gate, up, dh):
     out = [np.empty(g.shape, np.float64) for _ in range(3)]
     _load().mxref_swiglu_backward(pg, pu, pd, g.size, *[o.ctypes.data_as(ctypes.c_void_p) for o in out])
     return tuple(out)
+
+
+# ---- the one-GPU share of dispatch and combine (mxref.c states the readings) ----
+def route_plan(experts, G):
+    """experts int32 [T, k] -> (offsets int32 [G+1], src int32 [offsets[G]],
+    slot_of int32 [T, k]): a stable counting sort of the entries by expert."""
+    e, pe = _c(experts, np.int32)
+    T, k = e.shape
+    offsets = np.empty(G + 1, np.int32)
+    src = np.full(max(e.size, 1), -1, np.int32)
+    slot_of = np.empty((T, k), np.int32)
+    _load().mxref_route_plan(pe, e.size, k, G, offsets.ctypes.data_as(ctypes.c_void_p),
+                             src.ctypes.data_as(ctypes.c_void_p), slot_of.ctypes.data_as(ctypes.c_void_p))
+    return offsets, src[:offsets[G]], slot_of
+
+
+def f32_round(x):
+    return _load().mxref_f32_round(float(x))
+
+
+def gather_rows(x_bits, src, scale=None):
+    """bf16 bits [T, N], src int32 [M] (, float32 scale [M]) -> bf16 bits [M, N]."""
+    x, px = _c(x_bits, np.uint16)
+    s, ps = _c(src, np.int32)
+    T, N = x.shape
+    out = np.empty((s.size, N), np.uint16)
+    if scale is None:
+        pw = None
+    else:
+        w, pw = _c(scale, np.float32)
+        assert w.size == s.size
+    _load().mxref_gather_rows(px, T, N, ps, pw, s.size, out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def combine(y_bits, slot_of, w=None):
+    """bf16 bits [M, N], slot_of int32 [T, k] (, float32 w [T, k]) -> double [T, N]."""
+    y, py = _c(y_bits, np.uint16)
+    so, pso = _c(slot_of, np.int32)
+    M, N = y.shape
+    T, k = so.shape
+    if w is None:
+        pw = None
+    else:
+        wa, pw = _c(w, np.float32)
+        assert wa.shape == so.shape
+    out = np.empty((T, N), np.float64)
+    _load().mxref_combine(py, M, N, pso, pw, T, k, out.ctypes.data_as(ctypes.c_void_p))
+    return out

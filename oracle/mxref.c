@@ -373,3 +373,84 @@ void mxref_swiglu_backward(const double* gate, const double* up, const double* d
         h[i] = mxref_silu(gate[i]) * up[i];
     }
 }
+
+/* ---- the one-GPU share of dispatch and combine ----
+ * Readings (the MoK page, section 02, describes pull dispatch and push
+ * combine without formulas):
+ *   - a routed entry is a (token, choice) pair with an expert index; the
+ *     expert side lays its entries out grouped by expert and, inside an
+ *     expert, in entry order (token-major): a stable sort by expert;
+ *   - an entry whose expert index is outside [0, G) is not routed;
+ *   - combine is the routing-weighted sum of a token's expert outputs, the
+ *     usual top-k mixture; without weights the plain sum (the backward of the
+ *     gather);
+ *   - the scaled gather (the backward of the weighted combine: the output
+ *     gradient of a token times the entry's weight) is formed in binary32
+ *     and stored as bf16 before it is quantized. */
+void mxref_route_plan(const int32_t* experts, int64_t n, int32_t k, int32_t G, int32_t* offsets, int32_t* src,
+                      int32_t* slot_of) {
+    int64_t* cursor = calloc((size_t)G + 1, sizeof(int64_t));
+    for (int64_t j = 0; j < n; ++j)
+        if (experts[j] >= 0 && experts[j] < G) cursor[experts[j] + 1] += 1;
+    for (int32_t g = 0; g < G; ++g) cursor[g + 1] += cursor[g];
+    for (int32_t g = 0; g <= G; ++g) offsets[g] = (int32_t)cursor[g];
+    for (int64_t j = 0; j < n; ++j) {
+        const int32_t e = experts[j];
+        if (e < 0 || e >= G) {
+            slot_of[j] = -1;
+            continue;
+        }
+        const int64_t slot = cursor[e]++;
+        src[slot] = (int32_t)(j / k);
+        slot_of[j] = (int32_t)slot;
+    }
+    free(cursor);
+}
+
+double mxref_f32_round(double x) {
+    require_rne();
+    double a = fabs(x);
+    if (a == 0.0) return x;
+    int e;
+    (void)frexp(a, &e);
+    int E = e - 1;                                    /* floor(log2 a) */
+    if (E < -126) return copysign(ldexp(nearbyint(ldexp(a, 149)), -149), x);
+    double n = ldexp(nearbyint(ldexp(a, 23 - E)), E - 23);
+    if (n >= ldexp(1.0, 128)) return copysign(INFINITY, x);
+    return copysign(n, x);
+}
+
+void mxref_gather_rows(const uint16_t* x, int64_t T, int64_t N, const int32_t* src, const float* scale, int64_t M,
+                       uint16_t* out) {
+    for (int64_t r = 0; r < M; ++r) {
+        uint16_t* o = out + r * N;
+        if (src[r] < 0 || src[r] >= T) {
+            memset(o, 0, (size_t)N * sizeof(uint16_t));
+            continue;
+        }
+        const uint16_t* in = x + (int64_t)src[r] * N;
+        for (int64_t c = 0; c < N; ++c) {
+            if (scale == NULL) {
+                o[c] = in[c];
+            } else {
+                /* 24 x 8 significant bits: the double product is exact */
+                const double p = (double)scale[r] * mxref_bf16_value(in[c]);
+                o[c] = mxref_bf16_round(mxref_f32_round(p));
+            }
+        }
+    }
+}
+
+void mxref_combine(const uint16_t* y, int64_t M, int64_t N, const int32_t* slot_of, const float* w, int64_t T,
+                   int32_t k, double* out) {
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t c = 0; c < N; ++c) {
+            double acc = 0.0;
+            for (int32_t j = 0; j < k; ++j) {
+                const int32_t slot = slot_of[t * k + j];
+                if (slot < 0 || slot >= M) continue;
+                acc += (w ? (double)w[t * k + j] : 1.0) * mxref_bf16_value(y[(int64_t)slot * N + c]);
+            }
+            out[t * N + c] = acc;
+        }
+}

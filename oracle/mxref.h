@@ -114,6 +114,36 @@ void mxref_bf16_round_n(const double* x, int64_t n, uint16_t* out);
 void mxref_swiglu_backward(const double* gate, const double* up, const double* dh, int64_t n, double* dgate,
                            double* dup, double* h);
 
+/* The one-GPU share of expert-parallel dispatch and combine (kucoin.com MoK
+ * page, section 02: the expert side pulls each routed token by its source
+ * position and lays the rows out in local expert order; results go back to
+ * their tokens; MXFP8 is applied on the dispatch path).  The pages give no
+ * formulas; readings in mxref.c. */
+
+/* Stable counting sort of routed entries by expert.  experts[n] (n = T k,
+ * entry j = token j / k, choice j % k); entries outside [0, G) are dropped.
+ * offsets[G+1]: exclusive prefix of the per-expert counts; src[slot] = token
+ * of the entry placed there (slots ordered by expert, then by entry index);
+ * slot_of[j] = its slot, or -1 when dropped. */
+void mxref_route_plan(const int32_t* experts, int64_t n, int32_t k, int32_t G, int32_t* offsets, int32_t* src,
+                      int32_t* slot_of);
+
+/* Nearest-even binary32 value of x (subnormal quantum 2^-149, overflow to
+ * infinity), as a double. */
+double mxref_f32_round(double x);
+
+/* Gathered rows: out[r][:] = x[src[r]][:] (bf16 bit patterns), or, with a
+ * row scale, bf16(f32(scale[r] * x[src[r]][c])) (the product rounded to
+ * binary32, then to bf16, each to nearest even); rows with src[r] outside
+ * [0, T) are zero. */
+void mxref_gather_rows(const uint16_t* x, int64_t T, int64_t N, const int32_t* src, const float* scale, int64_t M,
+                       uint16_t* out);
+
+/* Combine: out[t][c] = sum_j w[t][j] y[slot_of[t][j]][c] over the entries
+ * whose slot lies in [0, M) (w == NULL: weight 1), in double. */
+void mxref_combine(const uint16_t* y, int64_t M, int64_t N, const int32_t* slot_of, const float* w, int64_t T,
+                   int32_t k, double* out);
+
 #ifdef __cplusplus
 }
 #endif

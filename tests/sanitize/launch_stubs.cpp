@@ -55,5 +55,18 @@ hipError_t launch_mfma_probe(const uint8_t*, const uint8_t*, const uint8_t*, con
                              int32_t, hipStream_t) {
     return hipErrorNotSupported;
 }
+hipError_t launch_route_plan(const int32_t*, const float*, int64_t, int32_t, int32_t, int32_t*, int32_t*, int32_t*,
+                             float*, hipStream_t) {
+    return hipErrorNotSupported;
+}
+hipError_t launch_gather_quantize(const uint16_t*, int64_t, int64_t, int64_t, const int32_t*, const float*, int64_t,
+                                  const int32_t*, int32_t, uint8_t*, uint8_t*, uint8_t*, uint8_t*, int64_t, int32_t*,
+                                  hipStream_t) {
+    return hipErrorNotSupported;
+}
+hipError_t launch_combine(const uint16_t*, int64_t, int64_t, int64_t, const int32_t*, const float*, int64_t, int32_t,
+                          uint16_t*, hipStream_t) {
+    return hipErrorNotSupported;
+}
 
 }  // namespace mx

@@ -150,6 +150,91 @@ def test_swiglu_backward_validation():
     assert f(None, None, 0, 64, None, None, None) == 0             # M == 0: no work
 
 
+def test_swiglu_backward_quant_validation():
+    f = mx.load().mx_swiglu_backward_quant
+    cap = mx.mx_cols_capacity(300, 3)
+    # (preact, dh, M, I, offsets, G, q, s, qT, sT, hT, hTs, Mcap, padded, stream)
+    ok = [FAKE, FAKE, 300, 128, FAKE, 3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, cap, FAKE, None]
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a3=96) == 5                        # I % 128 != 0
+    assert call(a2=-1) == 2                        # M < 0
+    assert call(a5=0) == 2                         # G < 1
+    assert call(a12=cap - 256) == 4                # capacity too small
+    assert call(a13=None) == 1                     # padded offsets required with groups
+    assert call(a0=None) == 1                      # NULL preact
+    assert call(a10=None) == 1                     # NULL h codes
+    assert call(a8=P(0x100004)) == 3               # misaligned column-wise codes
+    assert call(a0=None, a1=None, a2=0, a4=None, a6=None, a7=None, a3=0, a12=0, a13=None) == 0  # no work
+
+
+def test_route_plan_validation():
+    f = mx.load().mx_route_plan
+    # (experts, weights, T, k, G, offsets, src, slot_of, slot_weight, stream)
+    ok = [FAKE, None, 100, 8, 16, FAKE, FAKE, FAKE, None, None]
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a2=-1) == 2                        # T < 0
+    assert call(a3=0) == 2                         # k < 1
+    assert call(a4=0) == 2 and call(a4=4097) == 2  # G outside [1, 4096]
+    assert call(a2=1 << 28) == 5                   # T k >= 2^31
+    assert call(a5=None) == 1                      # NULL offsets
+    assert call(a0=None) == 1                      # NULL experts
+    assert call(a6=None) == 1                      # NULL src
+    assert call(a8=FAKE) == 1                      # slot weights without weights
+    assert call(a7=P(0x100002)) == 3               # misaligned slot_of
+
+
+def test_gather_quantize_validation():
+    f = mx.load().mx_gather_quantize
+    cap = mx.mx_cols_capacity(300, 3)
+    # (x, T, N, ldx, src, row_scale, M, offsets, G, q, s, qT, sT, Mcap, padded, stream)
+    ok = [FAKE, 50, 64, 64, FAKE, None, 300, FAKE, 3, FAKE, FAKE, FAKE, FAKE, cap, FAKE, None]
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a13=cap - 256) == 4                # capacity too small for M rows
+    assert call(a2=48, a3=64) == 2                 # N % 32 != 0
+    assert call(a1=-1) == 2                        # T < 0
+    assert call(a6=-1) == 2                        # M < 0
+    assert call(a3=32) == 2                        # ldx < N
+    assert call(a4=None) == 1                      # NULL src with rows
+    assert call(a0=None) == 1                      # NULL x with tokens
+    assert call(a14=None) == 1                     # padded offsets required with groups
+    assert call(a5=P(0x100002)) == 3               # misaligned row scale
+    assert call(a0=P(0x100008)) == 3               # misaligned x
+    assert call(a2=0, a7=None, a14=None) == 0      # N == 0, no groups: no work
+
+
+def test_combine_validation():
+    f = mx.load().mx_combine
+    # (y, M, N, ldy, slot_of, weights, T, k, out, stream)
+    ok = [FAKE, 800, 64, 64, FAKE, None, 100, 8, FAKE, None]
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a2=60, a3=64) == 5                 # N % 8 != 0
+    assert call(a3=32) == 2                        # ldy < N
+    assert call(a7=0) == 2                         # k < 1
+    assert call(a6=-1) == 2                        # T < 0
+    assert call(a4=None) == 1                      # NULL slot_of
+    assert call(a8=None) == 1                      # NULL out
+    assert call(a0=None) == 1                      # NULL y with rows
+    assert call(a8=P(0x100008)) == 3               # misaligned out
+    assert call(a5=P(0x100002)) == 3               # misaligned weights
+    assert call(a6=0, a4=None, a8=None) == 0       # no tokens: no work
+
+
 def test_validate_offsets_argument_errors():
     f = mx.load().mx_validate_offsets
     assert f(FAKE, 0, 100, FAKE, None) == 2        # G < 1

@@ -1,8 +1,9 @@
 """The oracle's pins must catch plausible mistakes.
 
 Each case plants one mistake in a private copy of oracle/mxref.c (on the CPU,
-in a temporary directory), builds it, and runs tests/test_oracle.py against
-that build in a subprocess: the pins must fail.  The oracle itself is never
+in a temporary directory), builds it, and runs tests/test_oracle.py (tests/test_oracle_routing.py for
+the dispatch and combine functions) against that build in a subprocess: the
+pins must fail.  The oracle itself is never
 modified.
 """
 import os
@@ -44,7 +45,19 @@ MUTANTS = {
     "bwd_dgate_no_up": ("dgate[i] = dh[i] * up[i] * mxref_dsilu(gate[i]);", "dgate[i] = dh[i] * mxref_dsilu(gate[i]);"),
     "bf16_round_truncates": ("double n = nearbyint(ldexp(a, 7 - E));", "double n = floor(ldexp(a, 7 - E));"),
     "bf16_subnormal_quantum": ("int n = (int)nearbyint(ldexp(a, 133));", "int n = (int)nearbyint(ldexp(a, 134));"),
+    # dispatch and combine (pinned in tests/test_oracle_routing.py)
+    "plan_unstable": ("    for (int64_t j = 0; j < n; ++j) {\n        const int32_t e = experts[j];\n        if (e < 0 || e >= G) {",
+                      "    for (int64_t j = n - 1; j >= 0; --j) {\n        const int32_t e = experts[j];\n        if (e < 0 || e >= G) {"),
+    "plan_keeps_last_expert_id": ("        if (e < 0 || e >= G) {\n            slot_of[j] = -1;",
+                                  "        if (e < 0 || e > G) {\n            slot_of[j] = -1;"),
+    "f32_subnormal_quantum": ("if (E < -126) return copysign(ldexp(nearbyint(ldexp(a, 149)), -149), x);",
+                              "if (E < -126) return copysign(ldexp(nearbyint(ldexp(a, 150)), -150), x);"),
+    "gather_single_rounding": ("o[c] = mxref_bf16_round(mxref_f32_round(p));", "o[c] = mxref_bf16_round(p);"),
+    "combine_ignores_weights": ("acc += (w ? (double)w[t * k + j] : 1.0) * mxref_bf16_value(y[(int64_t)slot * N + c]);",
+                                "acc += mxref_bf16_value(y[(int64_t)slot * N + c]);"),
 }
+ROUTING = {"plan_unstable", "plan_keeps_last_expert_id", "f32_subnormal_quantum", "gather_single_rounding",
+           "combine_ignores_weights"}
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -61,7 +74,8 @@ def test_pins_catch_planted_mistake(name):
         so = os.path.join(d, "libmxref_mutant.so")
         subprocess.check_call(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fPIC", "-shared", c, "-o", so, "-lm"])
         env = dict(os.environ, MXREF_LIB=so)
+        pins = "test_oracle_routing.py" if name in ROUTING else "test_oracle.py"
         r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                            os.path.join(ROOT, "tests", "test_oracle.py")],
+                            os.path.join(ROOT, "tests", pins)],
                            cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
         assert r.returncode != 0, f"mutant {name} survived the oracle pins"
