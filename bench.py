@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the MXFP8 hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--seed S] [--no-gemm] [--no-layer] [--no-layer-unfused] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--seed S] [--no-gemm] [--no-layer] [--no-layer-unfused]
+                    [--no-routed] [--no-cpu]
                     [--gemm-cases gate_up,swiglu,ragged,down] [--copy-calibration]
 
 Prints ONE JSON line.  The headline (``value``) is the quantize bandwidth on
@@ -27,7 +28,10 @@ that routing (quantize, gate+up GEMM with the quantizing SwiGLU epilogue, down
 GEMM; then dgrad, the SwiGLU backward fused with the quantization of its
 results, wgrad; weights re-quantized each step) and reports each stage's time
 and the quantize / GEMM time ratio, next to the same step with the SwiGLU
-backward and its quantizations as separate calls.
+backward and its quantizations as separate calls.  ``moe_layer_routed`` is one
+GPU's share of the expert-parallel layer: 4096 tokens routed top-8 to 16
+local experts, with the route plan, the dispatch (gather + MXFP8), the combine
+and their backward around the same expert computation.
 
 ``roofline`` describes the dominant kernel of the step (its own launch time
 from HIP events on the launch stream, next to the average of the committed
@@ -580,6 +584,86 @@ def bench_layer(torch, mx, W, args):
     return out
 
 
+def bench_routed(torch, mx, W, args):
+    """One GPU's share of an expert-parallel MoE layer: 4096 tokens routed
+    top-8 to 16 local experts (Dirichlet(0.5) expert popularity), H 7168,
+    I 2048; route plan, dispatch (gather + MXFP8), the expert computation,
+    combine, and their backward.  Per-stage GPU time from events between the
+    calls, the step timed without them, eagerly and as a HIP graph, and the
+    HBM rates of the dispatch and combine kernels (algorithmic bytes)."""
+    from mxfp8_block_scaled_04_amd.moe_layer import KIND, RoutedMoELayer
+
+    T, k, G, H, I = 4096, 8, 16, 7168, 2048
+    e, w = W.topk_routing(T, k, G, 0.5, args.seed)
+    ed, wd = torch.from_numpy(e).to("cuda"), torch.from_numpy(w).to("cuda")
+    X = W.normal_bf16((T, H), 1.0, args.seed + 101, "cuda")
+    dOut = W.normal_bf16((T, H), 1.0, args.seed + 102, "cuda")
+    W1 = mx.swiglu_interleave(W.normal_bf16((G, 2 * I, H), 0.02, args.seed + 103, "cuda"))
+    W2 = W.normal_bf16((G, H, I), 0.02, args.seed + 104, "cuda")
+    R = RoutedMoELayer(T, k, G, H, I)
+    step = lambda mark=None: R.step(X, dOut, ed, wd, W1, W2, mark)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    names, events = [], []
+
+    def mark(name):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record()
+        names.append(name)
+        events.append(ev)
+
+    stage = {}
+    for _ in range(args.steps):
+        names.clear()
+        events.clear()
+        mark("start")
+        step(mark)
+        events[-1].synchronize()
+        for i in range(1, len(events)):
+            stage[names[i]] = stage.get(names[i], 0.0) + events[i - 1].elapsed_time(events[i]) / args.steps
+    tm = Timer(torch)
+    ms_step = tm.run(step, args.steps)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    ms_graph = tm.run(graph.replay, args.steps)
+    del graph
+    M = T * k
+    # algorithmic HBM bytes: the gathered quantization reads M bf16 rows and
+    # writes both layouts (2 x (1 + 1/32) B per element); the combine reads
+    # the k expert rows of every token and writes its bf16 row
+    quant_bytes_ = 2 * M * H + 2 * M * H * (1 + 1 / 32)
+    comb_y_bytes = 2 * M * H + 2 * T * H
+    comb_dx_bytes = 2 * M * H + 2 * T * H
+    rate = lambda b, ms: b / (ms * 1e-3) / 1e12
+    kinds = {}
+    for n, ms in stage.items():
+        kinds[KIND[n]] = kinds.get(KIND[n], 0.0) + ms
+    out = {
+        "workload": f"routed MoE layer fwd+bwd, {T} tokens top-{k} of {G} local experts (Dirichlet(0.5) "
+                    f"popularity), H {H}, I {I}: {M} routed rows",
+        "ms_step": ms_step, "ms_step_graph": ms_graph, "tflops": R.flops() / (ms_step * 1e-3) / 1e12,
+        "ms_by_kind": kinds, "ms_by_stage": stage,
+        "tbs": {
+            "dispatch + quantize X": rate(quant_bytes_, stage["D dispatch + quantize X"]),
+            "reverse combine + quantize dOut": rate(quant_bytes_, stage["C' reverse combine + quantize dOut"]),
+            "combine": rate(comb_y_bytes, stage["C combine"]),
+            "reverse dispatch": rate(comb_dx_bytes, stage["D' reverse dispatch"]),
+        },
+    }
+    del R, X, dOut, W1, W2
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -588,6 +672,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-gemm", action="store_true", help="skip the grouped-GEMM section")
     ap.add_argument("--no-layer", action="store_true", help="skip the MoE-layer chain")
+    ap.add_argument("--no-routed", action="store_true", help="skip the routed MoE layer (dispatch and combine)")
     ap.add_argument("--no-layer-unfused", action="store_true",
                     help="skip the comparison step of the MoE layer with the SwiGLU backward unfused")
     ap.add_argument("--gemm-cases", default=",".join(GEMM_CASES),
@@ -622,6 +707,7 @@ def main():
     quant, sample = bench_quant(torch, mx, W, args)
     gemm = None if args.no_gemm else bench_gemm(torch, mx, W, args)
     layer = None if args.no_layer else bench_layer(torch, mx, W, args)
+    routed = None if args.no_layer or args.no_routed else bench_routed(torch, mx, W, args)
     cpu = None if sample is None else cpu_baseline(sample, args.seed, args.cpu_rows_1t)
 
     ms_step = quant["ms_rows"] + quant["ms_cols"]
@@ -700,6 +786,7 @@ def main():
         "quantize_dual": dict(quant["dual"], workload="bf16 [131072, 7168] -> row-wise + column-wise MXFP8, one read"),
         "gemm": gemm,
         "moe_layer": layer,
+        "moe_layer_routed": routed,
     }
     print(json.dumps(line), flush=True)
 

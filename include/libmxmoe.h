@@ -292,8 +292,9 @@ mx_status mx_swiglu_backward_quant(const uint16_t* preact, const uint16_t* dh, i
  *   slot_weight  NULL, or float [T k] out: weights[j] at slot_of[j] (needs
  *                weights; MX_ERR_NULL otherwise)
  * Requires T >= 0, k >= 1, 1 <= G <= 4096 (MX_ERR_SHAPE), T k < 2^31
- * (MX_ERR_UNSUPPORTED), 4-byte aligned pointers.  Two launches; the second
- * reads the expert list once per expert (O(G T k) reads, from L2).
+ * (MX_ERR_UNSUPPORTED), 4-byte aligned pointers.  Three launches (count,
+ * scan, place); the first and the last read the expert list once per expert
+ * (O(G T k) reads, from L2).
  */
 mx_status mx_route_plan(const int32_t* experts, const float* weights, int64_t T, int32_t k, int32_t G,
                         int32_t* offsets, int32_t* src, int32_t* slot_of, float* slot_weight, void* stream);

@@ -5,11 +5,11 @@
 // grouped by local expert, so that the grouped GEMM reads them in place; the
 // combine sends every expert output back to its token.  On one GPU the
 // source is local memory and the exchange is a gather:
-//  * route_count_kernel + route_place_kernel: a stable counting sort of the
-//    routed entries (token t, choice j) by expert, giving the group offsets,
-//    the source token of every expert-ordered slot and the slot of every
-//    entry (the gather itself, with MXFP8 on the way, is the gathering
-//    variant of the dual-layout quantizer);
+//  * route_count_kernel, route_scan_kernel, route_place_kernel: a stable
+//    counting sort of the routed entries (token t, choice j) by expert,
+//    giving the group offsets, the source token of every expert-ordered slot
+//    and the slot of every entry (the gather itself, with MXFP8 on the way,
+//    is the gathering variant of the dual-layout quantizer);
 //  * combine_kernel: out[t] = sum_j w[t][j] y[slot(t, j)], the routing-
 //    weighted sum of a token's expert outputs (the plain sum without weights:
 //    the backward of the gather).
@@ -21,34 +21,57 @@
 namespace mx {
 
 // ---------------------------------------------------------------------------
-// Routing plan, pass 1 (one workgroup of 1024 threads): per-expert counts
-// of the entries whose expert lies in [0, G) (LDS atomics: counts do not
-// depend on the order), their exclusive prefix into offsets[0..G], and
+// Routing plan, pass 1 (one workgroup of 1024 threads per expert): workgroup
+// g counts the entries of expert g (a ballot per 1024-entry piece, 8 pieces
+// loaded together, no atomics) into offsets[g + 1]; workgroup 0 also sets
 // slot -1 for the entries outside [0, G).
 // ---------------------------------------------------------------------------
-static_assert(kMaxGroups <= 4 * 1024, "the count kernel covers 4 experts per thread");
-__global__ __launch_bounds__(1024) void route_count_kernel(const int32_t* __restrict__ experts, int64_t n, int32_t G,
-                                                           int32_t* __restrict__ offsets,
-                                                           int32_t* __restrict__ slot_of) {
-    __shared__ int32_t cnt[kMaxGroups];
+constexpr int kPlanBatch = 8;  // entries per thread loaded together (their latencies overlap)
+constexpr int kPlanThreads = 1024;
+__global__ __launch_bounds__(kPlanThreads) void route_count_kernel(const int32_t* __restrict__ experts, int64_t n,
+                                                                   int32_t G, int32_t* __restrict__ offsets,
+                                                                   int32_t* __restrict__ slot_of) {
+    __shared__ int32_t wave_sum[kPlanThreads / 64];
+    const int t = threadIdx.x;
+    const int l = t & 63;
+    const int32_t g = (int32_t)blockIdx.x;
+    int32_t mine = 0;  // hits of this wave (lane 0)
+    for (int64_t c = 0; c < n; c += kPlanBatch * kPlanThreads) {
+        int32_t e[kPlanBatch];
+#pragma unroll
+        for (int b = 0; b < kPlanBatch; ++b) {
+            const int64_t j = c + b * kPlanThreads + t;
+            e[b] = j < n ? experts[j] : -1;
+        }
+#pragma unroll
+        for (int b = 0; b < kPlanBatch; ++b) {
+            mine += __popcll(__ballot(e[b] == g));
+            const int64_t j = c + b * kPlanThreads + t;
+            if (g == 0 && j < n && (e[b] < 0 || e[b] >= G)) slot_of[j] = -1;
+        }
+    }
+    if (l == 0) wave_sum[t >> 6] = mine;
+    __syncthreads();
+    if (t == 0) {
+        int32_t total = 0;
+        for (int w = 0; w < kPlanThreads / 64; ++w) total += wave_sum[w];
+        offsets[g + 1] = total;
+        if (g == 0) offsets[0] = 0;
+    }
+}
+
+// Routing plan, pass 2 (one workgroup): offsets[1..G] from counts to their
+// inclusive prefix, so offsets becomes the exclusive prefix of the counts.
+static_assert(kMaxGroups <= 4 * 1024, "the scan covers 4 experts per thread");
+__global__ __launch_bounds__(1024) void route_scan_kernel(int32_t G, int32_t* __restrict__ offsets) {
     __shared__ int32_t part[1024];
     const int t = threadIdx.x;
-    for (int g = t; g < G; g += 1024) cnt[g] = 0;
-    __syncthreads();
-    for (int64_t j = t; j < n; j += 1024) {
-        const int32_t e = experts[j];
-        if (e >= 0 && e < G)
-            atomicAdd(&cnt[e], 1);
-        else
-            slot_of[j] = -1;
-    }
-    __syncthreads();
     int32_t loc[4];
     int32_t sum = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int g = 4 * t + i;
-        loc[i] = g < G ? cnt[g] : 0;
+        loc[i] = g < G ? offsets[g + 1] : 0;
         sum += loc[i];
     }
     part[t] = sum;
@@ -63,55 +86,70 @@ __global__ __launch_bounds__(1024) void route_count_kernel(const int32_t* __rest
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int g = 4 * t + i;
-        if (g <= G) offsets[g] = run;
         run += loc[i];
+        if (g < G) offsets[g + 1] = run;
     }
-    if (t == 1023 && G == 4 * 1024) offsets[G] = run;
 }
 
 // ---------------------------------------------------------------------------
-// Routing plan, pass 2: workgroup g places the entries of expert g.  It
-// walks all entries in index order, 1024 at a time; a wave ballot gives each
-// hit its rank among the hits of its wave, a prefix over the 16 waves its
-// rank in the chunk, so slots follow the entry order (stable) and the result
-// does not depend on scheduling.  Each workgroup reads the whole expert list
+// Routing plan, pass 3: workgroup g places the entries of expert g.  It
+// walks all entries in index order, 8 x 1024 at a time (8 loads per thread
+// in flight); a wave ballot gives each hit its rank among the hits of its
+// wave and 1024-entry piece, a prefix over the pieces and waves before it
+// its rank in the batch, so slots follow the entry order (stable) and the
+// result does not depend on scheduling.  Each workgroup reads the whole expert list
 // (n ints, from L2): O(G n) reads in all, with an early exit once the
 // expert's count is placed.
 // ---------------------------------------------------------------------------
-constexpr int kPlaceThreads = 1024;
+constexpr int kPlaceThreads = kPlanThreads;
 __global__ __launch_bounds__(kPlaceThreads) void route_place_kernel(const int32_t* __restrict__ experts,
                                                                     const float* __restrict__ weights, int64_t n,
                                                                     int32_t k, const int32_t* __restrict__ offsets,
                                                                     int32_t* __restrict__ src,
                                                                     int32_t* __restrict__ slot_of,
                                                                     float* __restrict__ slot_weight) {
-    __shared__ int32_t wave_hits[kPlaceThreads / 64];
+    constexpr int kWaves = kPlaceThreads / 64;
+    constexpr int kPieces = kPlanBatch * kWaves;  // (1024-entry piece, wave) pairs of a batch, entry order
+    static_assert(kPieces <= kPlaceThreads, "one thread per pair in the prefix");
+    __shared__ int32_t hits[kPieces];
+    __shared__ int32_t prefix[kPieces + 1];
     const int t = threadIdx.x;
     const int w = t >> 6, l = t & 63;
     const int32_t g = (int32_t)blockIdx.x;
     int32_t base = offsets[g];
     const int32_t end = offsets[g + 1];
-    for (int64_t c = 0; c < n && base < end; c += kPlaceThreads) {
-        const int64_t j = c + t;
-        const bool hit = j < n && experts[j] == g;
-        const uint64_t mask = __ballot(hit);
-        if (l == 0) wave_hits[w] = __popcll(mask);
-        __syncthreads();
-        int32_t before = 0, total = 0;
+    for (int64_t c = 0; c < n && base < end; c += kPlanBatch * kPlaceThreads) {
+        bool hit[kPlanBatch];
 #pragma unroll
-        for (int v = 0; v < kPlaceThreads / 64; ++v) {
-            const int32_t h = wave_hits[v];
-            before += v < w ? h : 0;
-            total += h;
+        for (int b = 0; b < kPlanBatch; ++b) {
+            const int64_t j = c + b * kPlaceThreads + t;
+            hit[b] = j < n && experts[j] == g;
         }
-        if (hit) {
-            const int32_t slot = base + before + (int32_t)__popcll(mask & ((1ull << l) - 1ull));
+#pragma unroll
+        for (int b = 0; b < kPlanBatch; ++b) {
+            const uint64_t mask = __ballot(hit[b]);
+            if (l == 0) hits[b * kWaves + w] = __popcll(mask);
+        }
+        __syncthreads();
+        // exclusive prefix over the pairs (entry order: piece, then wave)
+        if (t <= kPieces) {
+            int32_t sum = 0;
+            for (int i = 0; i < t; ++i) sum += hits[i];
+            prefix[t] = sum;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < kPlanBatch; ++b) {
+            const uint64_t mask = __ballot(hit[b]);
+            if (!hit[b]) continue;
+            const int64_t j = c + b * kPlaceThreads + t;
+            const int32_t slot = base + prefix[b * kWaves + w] + (int32_t)__popcll(mask & ((1ull << l) - 1ull));
             src[slot] = (int32_t)(j / k);
             slot_of[j] = slot;
             if (slot_weight != nullptr) slot_weight[slot] = weights[j];
         }
-        base += total;
-        __syncthreads();  // wave_hits is rewritten by the next chunk
+        base += prefix[kPieces];
+        __syncthreads();  // hits and prefix are rewritten by the next batch
     }
 }
 
@@ -119,7 +157,9 @@ hipError_t launch_route_plan(const int32_t* experts, const float* weights, int64
                              int32_t* offsets, int32_t* src, int32_t* slot_of, float* slot_weight,
                              hipStream_t stream) {
     const int64_t n = T * k;
-    hipLaunchKernelGGL(route_count_kernel, dim3(1), dim3(1024), 0, stream, experts, n, G, offsets, slot_of);
+    hipLaunchKernelGGL(route_count_kernel, dim3((unsigned)G), dim3(kPlanThreads), 0, stream, experts, n, G, offsets,
+                       slot_of);
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, G, offsets);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || n == 0) return e;
     hipLaunchKernelGGL(route_place_kernel, dim3((unsigned)G), dim3(kPlaceThreads), 0, stream, experts, weights, n, k,

@@ -39,9 +39,9 @@ buffers once and issues the calls in order on the current stream
 """
 import torch
 
-from . import (mx_cols_capacity, mx_grouped_gemm, mx_grouped_gemm_dgrad, mx_grouped_gemm_swiglu,
-               mx_grouped_gemm_wgrad, mx_quantize_cols, mx_quantize_dual, mx_scale_bytes, mx_swiglu_backward,
-               mx_swiglu_backward_quant)
+from . import (mx_cols_capacity, mx_combine, mx_gather_quantize, mx_grouped_gemm, mx_grouped_gemm_dgrad,
+               mx_grouped_gemm_swiglu, mx_grouped_gemm_wgrad, mx_quantize_cols, mx_quantize_dual, mx_route_plan,
+               mx_scale_bytes, mx_swiglu_backward, mx_swiglu_backward_quant)
 
 FORWARD = ("F1 quantize X", "F2 gate+up GEMM + SwiGLU + quantize", "F3 down GEMM")
 BACKWARD = ("B1 quantize dY", "B2 down dgrad", "B3 SwiGLU backward + quantize", "B4 down wgrad",
@@ -49,7 +49,11 @@ BACKWARD = ("B1 quantize dY", "B2 down dgrad", "B3 SwiGLU backward + quantize", 
 BACKWARD_UNFUSED = ("B1 quantize dY", "B2 down dgrad", "B3a SwiGLU backward", "B3b quantize h (cols)",
                     "B3c quantize d(gate,up)", "B4 down wgrad", "B5 gate+up dgrad", "B6 gate+up wgrad")
 WEIGHTS = ("W1 quantize", "W2 quantize")
+ROUTED_FORWARD = ("R route plan", "D dispatch + quantize X", FORWARD[1], FORWARD[2], "C combine")
+ROUTED_BACKWARD = ("C' reverse combine + quantize dOut",) + BACKWARD[1:] + ("D' reverse dispatch",)
 KIND = {
+    "R route plan": "routing", "D dispatch + quantize X": "quant", "C combine": "routing",
+    "C' reverse combine + quantize dOut": "quant", "D' reverse dispatch": "routing",
     "F1 quantize X": "quant", "F2 gate+up GEMM + SwiGLU + quantize": "gemm", "F3 down GEMM": "gemm",
     "B1 quantize dY": "quant", "B2 down dgrad": "gemm", "B3 SwiGLU backward + quantize": "quant",
     "B3a SwiGLU backward": "elementwise", "B3b quantize h (cols)": "quant", "B3c quantize d(gate,up)": "quant",
@@ -127,9 +131,13 @@ class MoELayer:
         _mark(mark, "W2 quantize")
 
     def forward(self, X, mark=None):
-        G, H, I = self.G, self.H, self.I
         self.x.fill(X, self.offsets)
         _mark(mark, FORWARD[0])
+        return self.forward_experts(mark)
+
+    def forward_experts(self, mark=None):
+        """F2 and F3 on the quantized rows already in self.x."""
+        G, H, I = self.G, self.H, self.I
         mx_grouped_gemm_swiglu(self.x.q, self.x.s, self.w1.q.view(G, 2 * I, H), self.w1.s, self.offsets,
                                hq=self.hq, hs=self.hs, preact=self.preact)
         _mark(mark, FORWARD[1])
@@ -138,10 +146,15 @@ class MoELayer:
         return self.y
 
     def backward(self, dY, mark=None):
-        G = self.G
         names = BACKWARD if self.fused else BACKWARD_UNFUSED
         self.dy.fill(dY, self.offsets)
         _mark(mark, names[0])
+        return self.backward_experts(mark)
+
+    def backward_experts(self, mark=None):
+        """B2 to the end on the quantized output gradient already in self.dy."""
+        G = self.G
+        names = BACKWARD if self.fused else BACKWARD_UNFUSED
         mx_grouped_gemm_dgrad(self.dy.q, self.dy.s, self.w2.qT, self.w2.sT, self.offsets, G, out=self.dh)
         _mark(mark, names[1])
         if self.fused:
@@ -220,3 +233,67 @@ class MoELayer:
 def _mark(mark, name):
     if mark is not None:
         mark(name)
+
+
+class RoutedMoELayer:
+    """One GPU's share of an expert-parallel MoE layer: T tokens routed top-k
+    to G local experts (experts int32 [T, k], routing weights float32
+    [T, k]), dispatched, run through MoELayer's expert computation, and
+    combined (kucoin.com MoK page, section 02: pull dispatch into local expert
+    order, MXFP8 on the dispatch path, results pushed back to their tokens;
+    here the source is local memory and the exchange a gather).
+
+      R   route plan: offsets, slots, per-slot weights     mx_route_plan
+      D   dispatch: gather X rows by slot, quantize both ways (in place of
+          F1)                                              mx_gather_quantize
+      F2, F3 as MoELayer
+      C   combine: out[t] = sum_j w[t, j] y[slot(t, j)]     mx_combine
+      C'  reverse combine: gather dOut rows by slot, times the slot's
+          weight, quantize both ways (in place of B1)      mx_gather_quantize
+      B2 .. B6 as MoELayer
+      D'  reverse dispatch: dX[t] = sum_j dx[slot(t, j)]   mx_combine
+    The routing weights' own gradient (the router's) is not computed.
+    Every row of the layer's buffers is a slot (M = T k); entries routed to
+    an expert outside [0, G) are dropped."""
+
+    def __init__(self, T, k, G, H, I, device="cuda"):
+        self.T, self.k, self.G, self.H, self.I = T, k, G, H, I
+        self.offsets = torch.zeros(G + 1, dtype=torch.int32, device=device)
+        self.src = torch.empty(T * k, dtype=torch.int32, device=device)
+        self.slot_of = torch.empty((T, k), dtype=torch.int32, device=device)
+        self.slot_weight = torch.empty(T * k, dtype=torch.float32, device=device)
+        self.layer = MoELayer(self.offsets, T * k, H, I, device)
+        self.out = _bf16(T, H, device=device)
+        self.dX = _bf16(T, H, device=device)
+        self.stages = WEIGHTS + ROUTED_FORWARD + ROUTED_BACKWARD
+
+    def flops(self):
+        return self.layer.flops()
+
+    def forward(self, X, experts, weights, mark=None):
+        L = self.layer
+        mx_route_plan(experts, self.G, weights, self.offsets, self.src, self.slot_of, self.slot_weight)
+        _mark(mark, ROUTED_FORWARD[0])
+        x = L.x
+        mx_gather_quantize(X, self.src, L.M, self.offsets, x.Mcap, None, x.q, x.s, x.qT, x.sT, x.P)
+        _mark(mark, ROUTED_FORWARD[1])
+        L.forward_experts(mark)
+        mx_combine(L.y, self.slot_of, weights, out=self.out)
+        _mark(mark, ROUTED_FORWARD[4])
+        return self.out
+
+    def backward(self, dOut, mark=None):
+        L = self.layer
+        dy = L.dy
+        mx_gather_quantize(dOut, self.src, L.M, self.offsets, dy.Mcap, self.slot_weight, dy.q, dy.s, dy.qT, dy.sT,
+                           dy.P)
+        _mark(mark, ROUTED_BACKWARD[0])
+        L.backward_experts(mark)
+        mx_combine(L.dx, self.slot_of, None, out=self.dX)
+        _mark(mark, ROUTED_BACKWARD[-1])
+        return self.dX, L.dW1, L.dW2
+
+    def step(self, X, dOut, experts, weights, W1, W2, mark=None):
+        self.layer.quantize_weights(W1, W2, mark)
+        self.forward(X, experts, weights, mark)
+        return self.backward(dOut, mark)

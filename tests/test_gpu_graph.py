@@ -12,7 +12,7 @@ import torch
 
 import mxfp8_block_scaled_04_amd as mx
 from mxfp8_block_scaled_04_amd import workloads as W
-from mxfp8_block_scaled_04_amd.moe_layer import MoELayer
+from mxfp8_block_scaled_04_amd.moe_layer import MoELayer, RoutedMoELayer
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -72,3 +72,40 @@ def test_layer_step_graph_replays_match_eager(fuse, overlap):
         torch.cuda.synchronize()
         for k, v in outputs(layer).items():
             assert torch.equal(bits_of(v), bits_of(want[k])), f"replay {rep}: {k} differs from the eager step"
+
+
+def test_routed_layer_step_graph_replays_match_eager():
+    """The routed step (route plan, dispatch, experts, combine and their
+    backward) recorded once and replayed."""
+    T, k, G, H, I = 1024, 4, 8, 512, 256
+    e, w = W.topk_routing(T, k, G, 0.5, 26)
+    ed, wd = torch.from_numpy(e).to(DEV), torch.from_numpy(w).to(DEV)
+    X = W.normal_bf16((T, H), 1.0, 27, DEV)
+    dOut = W.normal_bf16((T, H), 1.0, 28, DEV)
+    W1 = mx.swiglu_interleave(W.normal_bf16((G, 2 * I, H), 1.2 / np.sqrt(H), 29, DEV))
+    W2 = W.normal_bf16((G, H, I), 1.2 / np.sqrt(I), 30, DEV)
+    R = RoutedMoELayer(T, k, G, H, I)
+    run = lambda: R.step(X, dOut, ed, wd, W1, W2)
+    res = lambda: {"out": R.out, "dX": R.dX, "dW1": R.layer.dW1, "dW2": R.layer.dW2, "src": R.src,
+                   "slot_of": R.slot_of, "offsets": R.offsets}
+    run()
+    torch.cuda.synchronize()
+    want = {n: v.clone() for n, v in res().items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in res().values():
+            t.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n, v in res().items():
+            assert torch.equal(bits_of(v), bits_of(want[n])), f"replay {rep}: {n} differs from the eager step"

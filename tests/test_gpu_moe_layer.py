@@ -14,8 +14,8 @@ import torch
 import mxfp8_block_scaled_04_amd as mx
 import oracle
 from mxfp8_block_scaled_04_amd import workloads as W
-from mxfp8_block_scaled_04_amd.moe_layer import BACKWARD, BACKWARD_UNFUSED, FORWARD, WEIGHTS, MoELayer
-from tests.mxtest import bf16_to_f64, bits, canonical_scales, gemm_tolerance_ok, u8
+from mxfp8_block_scaled_04_amd.moe_layer import BACKWARD, BACKWARD_UNFUSED, FORWARD, WEIGHTS, MoELayer, RoutedMoELayer
+from tests.mxtest import bf16_to_f64, bits, canonical_scales, combine_ok, gemm_tolerance_ok, u8
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -186,3 +186,44 @@ def test_moe_layer_overlapped_step_matches_the_sequential_one():
         for name in ("hq", "hT"):
             assert torch.equal(getattr(seq, name), getattr(ovl, name)), (rep, name)
         assert torch.equal(seq.dgu.q, ovl.dgu.q) and torch.equal(seq.dgu.qT, ovl.dgu.qT), rep
+
+
+def test_routed_layer_is_dispatch_experts_and_combine():
+    """The routed layer (600 tokens, top-4 of 8 experts): its plan against the
+    oracle; its expert side bit for bit equal to a plain MoELayer step on the
+    gathered token rows and the gathered, weight-scaled output gradient
+    (formed here with torch: an fp32 product rounded to bf16); its combined
+    output and token gradient against the oracle's combine."""
+    T, k, G, H, I = 600, 4, 8, 512, 256
+    e, w = W.topk_routing(T, k, G, 0.5, 41)
+    ed, wd = torch.from_numpy(e).to(DEV), torch.from_numpy(w).to(DEV)
+    X = W.normal_bf16((T, H), 1.0, 42, DEV)
+    dOut = W.normal_bf16((T, H), 1.0, 43, DEV)
+    W1 = mx.swiglu_interleave(W.normal_bf16((G, 2 * I, H), 1.2 / np.sqrt(H), 44, DEV))
+    W2 = W.normal_bf16((G, H, I), 0.05, 45, DEV)
+    R = RoutedMoELayer(T, k, G, H, I)
+    seen = []
+    R.step(X, dOut, ed, wd, W1, W2, mark=seen.append)
+    torch.cuda.synchronize()
+    assert seen == list(R.stages)
+    o_ref, s_ref, so_ref = oracle.route_plan(e, G)
+    assert np.array_equal(R.offsets.cpu().numpy(), o_ref) and np.array_equal(R.src.cpu().numpy(), s_ref)
+    assert np.array_equal(R.slot_of.cpu().numpy(), so_ref)
+
+    src = R.src.long()
+    Xg = X.index_select(0, src)
+    dYg = (dOut.index_select(0, src).float() * R.slot_weight[:, None]).to(torch.bfloat16)
+    plain = MoELayer(R.offsets.clone(), T * k, H, I)
+    plain.step(Xg, dYg, W1, W2)
+    torch.cuda.synchronize()
+    L = R.layer
+    for name in ("y", "dh", "dx", "dW1", "dW2", "preact"):
+        assert torch.equal(getattr(L, name).view(torch.int16), getattr(plain, name).view(torch.int16)), name
+    for name in ("q", "qT"):
+        assert torch.equal(getattr(L.x, name), getattr(plain.x, name)), name
+        assert torch.equal(getattr(L.dy, name), getattr(plain.dy, name)), name
+
+    ok, equal = combine_ok(bits(R.out), bits(L.y), so_ref, w)
+    assert ok, equal
+    ok, equal = combine_ok(bits(R.dX), bits(L.dx), so_ref, None)
+    assert ok, equal

@@ -12,7 +12,7 @@ import torch
 import mxfp8_block_scaled_04_amd as mx
 import oracle
 from mxfp8_block_scaled_04_amd import workloads as W
-from tests.mxtest import bits, canonical_scales, u8
+from tests.mxtest import bits, canonical_scales, combine_ok, u8
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -115,27 +115,15 @@ def test_gather_quantize_out_of_range_sources_are_zero_rows():
 
 
 def combine_check(out, y, slot_of, w, tokens=None):
-    """out bf16 [T, N] (or the rows `tokens`) against the oracle."""
-    yb = bits(y)
+    """out bf16 [T, N] (or its rows `tokens`) against the oracle."""
     so = slot_of.cpu().numpy()
     wh = None if w is None else w.cpu().numpy()
     if tokens is not None:
         so = so[tokens]
         wh = None if wh is None else wh[tokens]
-    exact = oracle.combine(yb, so, wh)
     got_b = bits(out) if tokens is None else bits(out[torch.from_numpy(tokens).to(DEV)])
-    got = (got_b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    yv = (yb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    k = so.shape[1]
-    mag = np.zeros_like(exact)
-    for j in range(k):
-        valid = so[:, j] >= 0
-        wj = np.ones(so.shape[0]) if wh is None else np.abs(wh[:, j]).astype(np.float64)
-        mag[valid] += wj[valid, None] * np.abs(yv[so[valid, j]])
-    bound = 2.0 ** -8 * np.abs(exact) + k * 2.0 ** -24 * mag + 2.0 ** -133
-    assert np.all(np.abs(got - exact) <= bound)
-    ref_b = oracle.bf16_round(exact)
-    assert np.mean(got_b == ref_b) >= 0.99
+    ok, equal = combine_ok(got_b, bits(y), so, wh)
+    assert ok, equal
 
 
 @pytest.mark.parametrize("T,k,G,N,weighted", [(500, 8, 16, 256, True), (500, 8, 16, 256, False),
