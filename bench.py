@@ -2,7 +2,7 @@
 """Benchmark of the MXFP8 hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--seed S] [--no-gemm] [--no-layer] [--no-layer-unfused]
-                    [--no-routed] [--no-cpu]
+                    [--no-routed] [--no-plain-layer] [--no-cpu]
                     [--gemm-cases gate_up,swiglu,ragged,down] [--copy-calibration]
 
 Prints ONE JSON line.  The headline (``value``) is the quantize bandwidth on
@@ -673,6 +673,8 @@ def main():
     ap.add_argument("--no-gemm", action="store_true", help="skip the grouped-GEMM section")
     ap.add_argument("--no-layer", action="store_true", help="skip the MoE-layer chain")
     ap.add_argument("--no-routed", action="store_true", help="skip the routed MoE layer (dispatch and combine)")
+    ap.add_argument("--no-plain-layer", action="store_true",
+                    help="skip the MoE layer on pre-grouped rows (the routed layer still runs)")
     ap.add_argument("--no-layer-unfused", action="store_true",
                     help="skip the comparison step of the MoE layer with the SwiGLU backward unfused")
     ap.add_argument("--gemm-cases", default=",".join(GEMM_CASES),
@@ -706,7 +708,7 @@ def main():
         torch.cuda.empty_cache()
     quant, sample = bench_quant(torch, mx, W, args)
     gemm = None if args.no_gemm else bench_gemm(torch, mx, W, args)
-    layer = None if args.no_layer else bench_layer(torch, mx, W, args)
+    layer = None if args.no_layer or args.no_plain_layer else bench_layer(torch, mx, W, args)
     routed = None if args.no_layer or args.no_routed else bench_routed(torch, mx, W, args)
     cpu = None if sample is None else cpu_baseline(sample, args.seed, args.cpu_rows_1t)
 

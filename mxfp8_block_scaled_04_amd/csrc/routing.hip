@@ -111,7 +111,9 @@ __global__ __launch_bounds__(kPlaceThreads) void route_place_kernel(const int32_
     constexpr int kWaves = kPlaceThreads / 64;
     constexpr int kPieces = kPlanBatch * kWaves;  // (1024-entry piece, wave) pairs of a batch, entry order
     static_assert(kPieces <= kPlaceThreads, "one thread per pair in the prefix");
+    static_assert(kPieces == 128, "the prefix scan below covers two waves of pairs");
     __shared__ int32_t hits[kPieces];
+    __shared__ int32_t incl[kPieces];
     __shared__ int32_t prefix[kPieces + 1];
     const int t = threadIdx.x;
     const int w = t >> 6, l = t & 63;
@@ -131,12 +133,21 @@ __global__ __launch_bounds__(kPlaceThreads) void route_place_kernel(const int32_
             if (l == 0) hits[b * kWaves + w] = __popcll(mask);
         }
         __syncthreads();
-        // exclusive prefix over the pairs (entry order: piece, then wave)
-        if (t <= kPieces) {
-            int32_t sum = 0;
-            for (int i = 0; i < t; ++i) sum += hits[i];
-            prefix[t] = sum;
+        // exclusive prefix over the pairs (entry order: piece, then wave):
+        // an inclusive scan inside each of the first two waves by lane
+        // shifts, then wave 1 adds wave 0's total
+        if (t < kPieces) {
+            int32_t v = hits[t];
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int32_t u = __shfl_up(v, d);
+                if (l >= d) v += u;
+            }
+            incl[t] = v;
         }
+        __syncthreads();
+        if (t < kPieces) prefix[t] = incl[t] - hits[t] + (t >= 64 ? incl[63] : 0);
+        if (t == kPieces) prefix[t] = incl[63] + incl[127];
         __syncthreads();
 #pragma unroll
         for (int b = 0; b < kPlanBatch; ++b) {
