@@ -97,9 +97,9 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t G, int32_t* __
 // in flight); a wave ballot gives each hit its rank among the hits of its
 // wave and 1024-entry piece, a prefix over the pieces and waves before it
 // its rank in the batch, so slots follow the entry order (stable) and the
-// result does not depend on scheduling.  Each workgroup reads the whole expert list
-// (n ints, from L2): O(G n) reads in all, with an early exit once the
-// expert's count is placed.
+// result does not depend on scheduling.  Each workgroup reads the whole
+// expert list (n ints, from L2): O(G n) reads in all, with an early exit once
+// the expert's count is placed.
 // ---------------------------------------------------------------------------
 constexpr int kPlaceThreads = kPlanThreads;
 __global__ __launch_bounds__(kPlaceThreads) void route_place_kernel(const int32_t* __restrict__ experts,
