@@ -658,7 +658,10 @@ def bench_routed(torch, mx, W, args):
             "combine": rate(comb_y_bytes, stage["C combine"]),
             "reverse dispatch": rate(comb_dx_bytes, stage["D' reverse dispatch"]),
         },
+        "tbs_note": "algorithmic bytes / stage time (the stage includes the launch gaps around its kernels); "
+                    "frac_hbm_peak divides by 8 TB/s",
     }
+    out["frac_hbm_peak"] = {n: v / HBM_PEAK_TBS for n, v in out["tbs"].items()}
     del R, X, dOut, W1, W2
     torch.cuda.empty_cache()
     return out
