@@ -71,6 +71,15 @@ def pipeline(d, off):
     Mcap = qT.shape[1]
     canon = lambda t, R, C: torch.from_numpy(oracle.unpack_scales(t.cpu().numpy(), R, C))
     out["swiglu_bwd_quant"] = (q, qT, hT, P2, canon(s, M, 2 * N), canon(sT, 2 * N, Mcap), canon(hTs, N, Mcap))
+    # dispatch and combine: 128 tokens routed top-2 to the 4 experts
+    e, wts = W.topk_routing(128, 2, G, 0.5, 8)
+    ed, wd = torch.from_numpy(e).to(DEV), torch.from_numpy(wts).to(DEV)
+    offs, src, slot_of, slot_w = mx.mx_route_plan(ed, G, wd)
+    Mr = 256
+    gq = mx.mx_gather_quantize(x[:128], src, Mr, offs, None, slot_w)
+    McapR = gq[2].shape[1]
+    out["routing"] = (offs, src, slot_of, slot_w, gq[0], gq[2], gq[4], canon(gq[1], Mr, K), canon(gq[3], K, McapR),
+                      mx.mx_combine(x[:Mr], slot_of, wd))
     # backward of a projection with 256 outputs (dgrad contracts over them)
     N2 = 256
     w2 = W.normal_bf16((G, N2, K), 0.05, 6, DEV)
