@@ -186,6 +186,7 @@ hipError_t launch_route_plan(const int32_t* experts, const float* weights, int64
 // (not routed) are skipped; without weights every entry counts once.
 // ---------------------------------------------------------------------------
 constexpr int kCombineThreads = 256;
+constexpr int kCombineGroup = 8;  // entries whose rows are loaded together
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t* __restrict__ y, int64_t M,
                                                                   int64_t N, int64_t ldy,
                                                                   const int32_t* __restrict__ slot_of,
@@ -195,16 +196,33 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const uint16_t
     const int64_t c0 = ((int64_t)blockIdx.y * kCombineThreads + threadIdx.x) * 8;
     if (c0 >= N) return;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int32_t j = 0; j < k; ++j) {
-        const int32_t slot = slot_of[tok * k + j];
-        if (slot < 0 || slot >= M) continue;
-        const float wj = w != nullptr ? w[tok * k + j] : 1.0f;
-        const uint4 v = load_stream16(y + (int64_t)slot * ldy + c0);
-        const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+    // the entries in groups of 8: all their row loads in flight at once,
+    // then the sums in choice order
+    for (int32_t j0 = 0; j0 < k; j0 += kCombineGroup) {
+        uint4 v[kCombineGroup];
+        float wv[kCombineGroup];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[2 * i] = __builtin_fmaf(wj, lo_bf16(vw[i]), acc[2 * i]);
-            acc[2 * i + 1] = __builtin_fmaf(wj, hi_bf16(vw[i]), acc[2 * i + 1]);
+        for (int u = 0; u < kCombineGroup; ++u) {
+            const int32_t j = j0 + u;
+            const int32_t slot = j < k ? slot_of[tok * k + j] : -1;
+            wv[u] = 0.0f;
+            v[u] = make_uint4(0, 0, 0, 0);
+            if (slot >= 0 && slot < M) {
+                wv[u] = w != nullptr ? w[tok * k + j] : 1.0f;
+                v[u] = load_stream16(y + (int64_t)slot * ldy + c0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kCombineGroup; ++u) {
+            if (j0 + u >= k) break;
+            const int32_t slot = slot_of[tok * k + j0 + u];
+            if (slot < 0 || slot >= M) continue;
+            const uint32_t vw[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] = __builtin_fmaf(wv[u], lo_bf16(vw[i]), acc[2 * i]);
+                acc[2 * i + 1] = __builtin_fmaf(wv[u], hi_bf16(vw[i]), acc[2 * i + 1]);
+            }
         }
     }
     store16(out + tok * N + c0, make_uint4(pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]),
