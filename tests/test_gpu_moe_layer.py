@@ -227,3 +227,45 @@ def test_routed_layer_is_dispatch_experts_and_combine():
     assert ok, equal
     ok, equal = combine_ok(bits(R.dX), bits(L.dx), so_ref, None)
     assert ok, equal
+
+
+def test_routed_layer_with_dropped_entries_and_empty_experts():
+    """Routing where experts 1, 4 and 6 get no token and about 10 % of the
+    entries name no expert (-1): the routed rows are the first offsets[G]
+    slots; their expert side equals a plain MoELayer over just those rows,
+    the weight gradients of the empty experts are zero, and the combines skip
+    the dropped entries."""
+    T, k, G, H, I = 500, 4, 8, 512, 256
+    rng = np.random.default_rng(51)
+    e = rng.choice([0, 2, 3, 5, 7], (T, k)).astype(np.int32)
+    e[rng.random((T, k)) < 0.1] = -1
+    w = rng.uniform(0, 1, (T, k)).astype(np.float32)
+    ed, wd = torch.from_numpy(e).to(DEV), torch.from_numpy(w).to(DEV)
+    X = W.normal_bf16((T, H), 1.0, 52, DEV)
+    dOut = W.normal_bf16((T, H), 1.0, 53, DEV)
+    W1 = mx.swiglu_interleave(W.normal_bf16((G, 2 * I, H), 1.2 / np.sqrt(H), 54, DEV))
+    W2 = W.normal_bf16((G, H, I), 0.05, 55, DEV)
+    R = RoutedMoELayer(T, k, G, H, I)
+    R.step(X, dOut, ed, wd, W1, W2)
+    torch.cuda.synchronize()
+    o_ref, s_ref, so_ref = oracle.route_plan(e, G)
+    Mr = int(o_ref[-1])
+    assert Mr < T * k and np.array_equal(R.offsets.cpu().numpy(), o_ref)
+    assert np.array_equal(R.slot_of.cpu().numpy(), so_ref)
+
+    src = R.src[:Mr].long()
+    plain = MoELayer(R.offsets.clone(), Mr, H, I)
+    plain.step(X.index_select(0, src),
+               (dOut.index_select(0, src).float() * R.slot_weight[:Mr, None]).to(torch.bfloat16), W1, W2)
+    torch.cuda.synchronize()
+    L = R.layer
+    for name in ("y", "dh", "dx", "preact"):
+        assert torch.equal(getattr(L, name)[:Mr].view(torch.int16), getattr(plain, name).view(torch.int16)), name
+    for name in ("dW1", "dW2"):
+        assert torch.equal(getattr(L, name).view(torch.int16), getattr(plain, name).view(torch.int16)), name
+    for g in (1, 4, 6):
+        assert not L.dW1[g].abs().sum() and not L.dW2[g].abs().sum(), g
+    ok, equal = combine_ok(bits(R.out), bits(L.y[:Mr]), so_ref, w)
+    assert ok, equal
+    ok, equal = combine_ok(bits(R.dX), bits(L.dx[:Mr]), so_ref, None)
+    assert ok, equal
