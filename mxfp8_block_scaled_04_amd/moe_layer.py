@@ -1,6 +1,8 @@
 """One MoE layer's expert computation on one GPU, forward and backward, as a
-chain of libmxmoe calls (no router and no dispatch/combine: the token rows
-arrive grouped by expert).  This is the layer-level view of the public
+chain of libmxmoe calls.  MoELayer takes token rows already grouped by
+expert; RoutedMoELayer (at the end) adds the route plan, the dispatch and the
+combine around it for top-k routed tokens (no router: the expert choices and
+weights are inputs).  This is the layer-level view of the public
 write-ups on Cursor's MXFP8 MoE kernels (aigc.bar "被忽视的量化税": the
 quantization passes next to the grouped GEMMs of a layer; lpnh.cn 2479732
 section 1: the forward and backward passes and the transposed quantization
