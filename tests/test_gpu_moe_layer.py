@@ -269,3 +269,31 @@ def test_routed_layer_with_dropped_entries_and_empty_experts():
     assert ok, equal
     ok, equal = combine_ok(bits(R.dX), bits(L.dx[:Mr]), so_ref, None)
     assert ok, equal
+
+
+def test_routed_layer_at_full_size_equals_the_plain_layer():
+    """The routed layer at the benchmark's shape (4096 tokens top-8 of 16
+    experts, H 7168, I 2048): its expert side, bit for bit, equals a plain
+    MoELayer step on the gathered rows and the gathered, weight-scaled output
+    gradient."""
+    T, k, G, H, I = 4096, 8, 16, 7168, 2048
+    e, w = W.topk_routing(T, k, G, 0.5, 61)
+    ed, wd = torch.from_numpy(e).to(DEV), torch.from_numpy(w).to(DEV)
+    X = W.normal_bf16((T, H), 1.0, 62, DEV)
+    dOut = W.normal_bf16((T, H), 1.0, 63, DEV)
+    W1 = mx.swiglu_interleave(W.normal_bf16((G, 2 * I, H), 0.02, 64, DEV))
+    W2 = W.normal_bf16((G, H, I), 0.02, 65, DEV)
+    R = RoutedMoELayer(T, k, G, H, I)
+    R.step(X, dOut, ed, wd, W1, W2)
+    torch.cuda.synchronize()
+    src = R.src.long()
+    plain = MoELayer(R.offsets.clone(), T * k, H, I)
+    plain.step(X.index_select(0, src),
+               (dOut.index_select(0, src).float() * R.slot_weight[:, None]).to(torch.bfloat16), W1, W2)
+    torch.cuda.synchronize()
+    L = R.layer
+    for name in ("y", "dh", "dx", "dW1", "dW2", "preact"):
+        assert torch.equal(getattr(L, name).view(torch.int16), getattr(plain, name).view(torch.int16)), name
+    for name in ("q", "s", "qT", "sT"):
+        assert torch.equal(getattr(L.x, name), getattr(plain.x, name)), name
+        assert torch.equal(getattr(L.dy, name), getattr(plain.dy, name)), name
