@@ -330,7 +330,7 @@ mx_status mx_gather_quantize(const uint16_t* x, int64_t T, int64_t N, int64_t ld
  *   out      bf16 [T][N], written in full
  * Requires N % 8 == 0 (MX_ERR_UNSUPPORTED), ldy >= N, k >= 1 (MX_ERR_SHAPE),
  * y, out 16-byte aligned, ldy % 8 == 0, slot_of and weights 4-byte aligned
- * (MX_ERR_ALIGN); T < 2^31, N / 2048 < 65536 (MX_ERR_UNSUPPORTED).
+ * (MX_ERR_ALIGN); T < 2^24, N / 2048 < 65536 (MX_ERR_UNSUPPORTED).
  */
 mx_status mx_combine(const uint16_t* y, int64_t M, int64_t N, int64_t ldy, const int32_t* slot_of,
                      const float* weights, int64_t T, int32_t k, uint16_t* out, void* stream);

@@ -283,7 +283,9 @@ mx_status mx_combine(const uint16_t* y, int64_t M, int64_t N, int64_t ldy, const
     if ((y && !aligned16(y)) || !aligned16(out) || ldy % 8 != 0 || !aligned4(slot_of) ||
         (weights && !aligned4(weights)))
         return MX_ERR_ALIGN;
-    if (T > (int64_t)INT32_MAX || (N / 8 + 255) / 256 > 65535) return MX_ERR_UNSUPPORTED;  // grid
+    // grid: T workgroups of 256 lanes (the combine kernel's size; total
+    // work-items < 2^32) by N / 2048
+    if (T > (int64_t)(UINT32_MAX / 256) || (N / 8 + 255) / 256 > 65535) return MX_ERR_UNSUPPORTED;
     return from_hip(mx::launch_combine(y, M, N, ldy, slot_of, weights, T, k, out, (hipStream_t)stream));
 }
 

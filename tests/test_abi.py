@@ -233,6 +233,8 @@ def test_combine_validation():
     assert call(a8=P(0x100008)) == 3               # misaligned out
     assert call(a5=P(0x100002)) == 3               # misaligned weights
     assert call(a6=0, a4=None, a8=None) == 0       # no tokens: no work
+    assert call(a6=1 << 24) == 5                   # T workgroups of 256 lanes: 2^32 work-items
+    assert call(a2=8 * 256 * 65536, a3=8 * 256 * 65536) == 5  # N / 2048 columns blocks >= 65536
 
 
 def test_validate_offsets_argument_errors():
