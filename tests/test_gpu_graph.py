@@ -109,3 +109,44 @@ def test_routed_layer_step_graph_replays_match_eager():
         torch.cuda.synchronize()
         for n, v in res().items():
             assert torch.equal(bits_of(v), bits_of(want[n])), f"replay {rep}: {n} differs from the eager step"
+
+
+def test_routed_layer_graph_follows_new_routing():
+    """One capture serves every routing of the same shape: the plan, the
+    group offsets and the slots are computed on the device from the expert
+    ids the graph reads, so rewriting the ids and weights in place between
+    replays must give the eager step on the new routing, bit for bit."""
+    T, k, G, H, I = 1024, 4, 8, 512, 256
+    routings = [W.topk_routing(T, k, G, a, s) for a, s in ((0.5, 40), (0.1, 41), (5.0, 42))]
+    X = W.normal_bf16((T, H), 1.0, 43, DEV)
+    dOut = W.normal_bf16((T, H), 1.0, 44, DEV)
+    W1 = mx.swiglu_interleave(W.normal_bf16((G, 2 * I, H), 1.2 / np.sqrt(H), 45, DEV))
+    W2 = W.normal_bf16((G, H, I), 1.2 / np.sqrt(I), 46, DEV)
+    ed = torch.from_numpy(routings[0][0]).to(DEV)
+    wd = torch.from_numpy(routings[0][1]).to(DEV)
+    R = RoutedMoELayer(T, k, G, H, I)
+    ref = RoutedMoELayer(T, k, G, H, I)
+    run = lambda: R.step(X, dOut, ed, wd, W1, W2)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    for e, w in routings[1:] + routings[:1]:
+        ed.copy_(torch.from_numpy(e))
+        wd.copy_(torch.from_numpy(w))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref.step(X, dOut, ed, wd, W1, W2)
+        torch.cuda.synchronize()
+        assert torch.equal(R.offsets, ref.offsets) and torch.equal(R.slot_of, ref.slot_of)
+        for name in ("out", "dX"):
+            assert torch.equal(bits_of(getattr(R, name)), bits_of(getattr(ref, name))), name
+        for name in ("dW1", "dW2"):
+            assert torch.equal(bits_of(getattr(R.layer, name)), bits_of(getattr(ref.layer, name))), name
