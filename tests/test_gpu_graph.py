@@ -150,3 +150,42 @@ def test_routed_layer_graph_follows_new_routing():
             assert torch.equal(bits_of(getattr(R, name)), bits_of(getattr(ref, name))), name
         for name in ("dW1", "dW2"):
             assert torch.equal(bits_of(getattr(R.layer, name)), bits_of(getattr(ref.layer, name))), name
+
+
+def test_layer_graph_follows_new_group_sizes():
+    """The plain layer's capture reads the group offsets from device memory:
+    new group sizes written in place between replays (an empty group, a
+    one-row group, a single group) must give the eager step on them, bit for
+    bit, in every output that the step writes in full."""
+    M, H, I, G = 4096, 512, 256, 8
+    size_sets = [W.dirichlet_sizes(M, G, 0.5, 31), [0, 1, 2047, 0, 1000, 31, 33, 984],
+                 [0, 0, 0, M, 0, 0, 0, 0], W.dirichlet_sizes(M, G, 5.0, 32)]
+    off = torch.from_numpy(W.offsets_from_sizes(size_sets[0])).to(DEV)
+    X = W.normal_bf16((M, H), 1.0, 33, DEV)
+    dY = W.normal_bf16((M, H), 1.0, 34, DEV)
+    W1 = mx.swiglu_interleave(W.normal_bf16((G, 2 * I, H), 1.2 / np.sqrt(H), 35, DEV))
+    W2 = W.normal_bf16((G, H, I), 1.2 / np.sqrt(I), 36, DEV)
+    layer = MoELayer(off, M, H, I)
+    ref = MoELayer(off, M, H, I)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.step(X, dY, W1, W2)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer.step(X, dY, W1, W2)
+    torch.cuda.synchronize()
+    full = ("y", "dx", "dW1", "dW2", "hq", "preact", "dh")
+    for sizes in size_sets[1:] + size_sets[:1]:
+        assert sum(sizes) == M
+        off.copy_(torch.from_numpy(W.offsets_from_sizes(sizes)))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref.step(X, dY, W1, W2)
+        torch.cuda.synchronize()
+        for name in full:
+            assert torch.equal(bits_of(getattr(layer, name)), bits_of(getattr(ref, name))), (sizes, name)
+        assert torch.equal(layer.dgu.q, ref.dgu.q), sizes
